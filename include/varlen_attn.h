@@ -1,0 +1,226 @@
+/*
+ * varlen_attn.h -- C ABI of the MI355X (gfx950) packed variable-length
+ * scaled-dot-product attention library (libvarlen_attn.so).
+ *
+ * Source pages (crate onnx-runtime-ep-cuda, docs.rs source view):
+ *   [PVA] src/kernels/packed_varlen_attention.rs, 0.1.0-dev.6
+ *   [STD] src/kernels/standard_attention.rs, latest page
+ *   [GQA] src/kernels/group_query_attention.rs, latest page
+ *
+ * What the library computes ([PVA] module doc "Packed layout & cumulative
+ * offsets", "Schema (v1)", "Causal alignment"; [STD] module doc "Semantics"):
+ * B sequences are concatenated on one token axis. Sequence b owns query rows
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key/value rows
+ * [cu_seqlens_kv[b], cu_seqlens_kv[b+1]); nothing attends across sequences.
+ * For query head h the kv head is h / (num_heads / kv_num_heads). Scores are
+ * scale * (q . k) (the pages fold sqrt(scale) into each operand; that is the
+ * same number), then softcap * tanh(s / softcap) when softcap != 0, then the
+ * tail-aligned causal mask (query i sees key j iff j <= i + L_kv - L_q), then
+ * a stable softmax over the visible keys; a row that sees no key is all
+ * zeros. out = softmax . V, accumulated in fp32, stored in the I/O type with
+ * round-to-nearest-even.
+ *
+ * Conventions shared by every entry point:
+ *  - Device pointers are HIP device addresses on the current device; host
+ *    pointers are ordinary host memory. The library never takes ownership of
+ *    a caller's buffer.
+ *  - Every argument is validated on the host before any device work is
+ *    enqueued; on failure nothing is launched, `out` is untouched, a status
+ *    other than VARLEN_OK is returned, and varlen_attn_last_error() holds a
+ *    message that begins "varlen_attn_fwd: " (in the spirit of the pages'
+ *    op-prefixed KernelFailed errors, [PVA] error helper and execute()).
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    null stream) and the call returns without synchronizing, except for the
+ *    one case documented at varlen_attn_fwd.
+ */
+#ifndef VARLEN_ATTN_H_
+#define VARLEN_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of Q, K, V and out ([PVA] "Schema (v1)": f32, f16 or bf16,
+ * the same for all four). */
+typedef enum {
+  VARLEN_F32 = 0,
+  VARLEN_F16 = 1,
+  VARLEN_BF16 = 2
+} varlen_dtype_t;
+
+typedef enum {
+  VARLEN_OK = 0,
+  /* null pointer, num_heads <= 0, kv_num_heads does not divide num_heads,
+   * head_dim <= 0, negative or non-finite scale, non-finite softcap, bad
+   * dtype code, total_q/total_kv out of range */
+  VARLEN_ERR_INVALID_ARGUMENT = 1,
+  /* batch < 1, cu[0] != 0, a decreasing cu array, cu[batch] != total
+   * ([PVA] execute(): cumulative-array validation) */
+  VARLEN_ERR_BAD_SEQLENS = 2,
+  /* a dtype / head_dim combination that has no GPU kernel */
+  VARLEN_ERR_UNSUPPORTED = 3,
+  /* a HIP runtime error (the message carries hipGetErrorString) */
+  VARLEN_ERR_DEVICE = 4,
+  VARLEN_ERR_OUT_OF_MEMORY = 5
+} varlen_status_t;
+
+/*
+ * varlen_attn_fwd -- packed varlen attention forward ([PVA] the op's
+ * execute(); numerics [PVA] "Numerics & determinism").
+ *
+ *  q              device, contiguous [total_q, num_heads, head_dim]
+ *                 (a [total_q, num_heads*head_dim] tensor has the same bytes)
+ *  k              device, contiguous [total_kv, kv_num_heads, head_dim]
+ *  v              device, contiguous [total_kv, kv_num_heads, v_head_dim]
+ *  cu_seqlens_q   device int32 [batch+1]; may be NULL when the host mirror
+ *                 is given
+ *  cu_seqlens_kv  device int32 [batch+1]; may be NULL when the host mirror
+ *                 is given
+ *  cu_seqlens_q_host, cu_seqlens_kv_host
+ *                 optional host mirrors of the same arrays. When both are
+ *                 given the device arrays are not read at all. When either
+ *                 is NULL the library copies the device arrays to the host
+ *                 on `stream` and waits for that stream (the only
+ *                 synchronizing case, as the pages' op reads cu_seqlens back
+ *                 before it launches: [PVA] read_cu_seqlens).
+ *  batch          B >= 1
+ *  total_q        packed query tokens (rows of q and out), 0 allowed
+ *  total_kv       packed key/value tokens
+ *  num_heads      Hq >= 1
+ *  kv_num_heads   Hkv; <= 0 means Hkv = Hq; must divide Hq
+ *  head_dim       D of q and k
+ *  v_head_dim     Dv of v and out; <= 0 means Dv = D
+ *  dtype          varlen_dtype_t of q, k, v and out
+ *  scale          0 selects 1/sqrt(head_dim); otherwise > 0 and finite
+ *  is_causal      0 or non-zero (tail-aligned causal mask)
+ *  softcap        0 disables; any other finite value c applies
+ *                 c * tanh(s / c) (c and -c give the same function)
+ *  out            device, caller-allocated [total_q, num_heads, v_head_dim]
+ *                 of dtype; every element is written
+ *  stream         hipStream_t as void*
+ *
+ * GPU kernels exist for: bf16 and f16 with head_dim == v_head_dim in
+ * {64, 128}; f32 with head_dim, v_head_dim <= 128. Anything else returns
+ * VARLEN_ERR_UNSUPPORTED.
+ *
+ * Buffers q, k, v, the cu arrays and out are borrowed and must stay valid
+ * until the enqueued work completes. The library keeps a grow-only
+ * per-device workspace (work lists, split-KV partials) and serialises calls
+ * that use it: a call on another stream waits (on the device) for the
+ * previous call's kernels. Results are deterministic run to run: no
+ * floating-point atomics, fixed reduction orders.
+ */
+varlen_status_t varlen_attn_fwd(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                const int32_t* cu_seqlens_q_host,
+                                const int32_t* cu_seqlens_kv_host, int32_t batch,
+                                int64_t total_q, int64_t total_kv, int32_t num_heads,
+                                int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                                int32_t dtype, float scale, int32_t is_causal, float softcap,
+                                void* out, void* stream);
+
+/*
+ * Options that steer how the work is split, for tests that prove the paths
+ * agree and for tuning. Passing NULL options to varlen_attn_fwd_ex is the
+ * same as varlen_attn_fwd. The result is the same for every option value up
+ * to fp32 rounding.
+ *
+ *  decode_path    0 auto (split-KV decode kernel for sequences with L_q == 1
+ *                 on bf16/f16), 1 never (every sequence through the prefill
+ *                 kernel), 2 same as auto
+ *  decode_chunk   keys per split-KV work item; 0 picks automatically
+ *                 (rounded up to a multiple of 128)
+ *  prefill_kv_chunk  keys per prefill work item when long key ranges are
+ *                 split across workgroups and recombined by the log-sum-exp
+ *                 combine; 0 picks automatically, < 0 never splits
+ */
+typedef struct {
+  int32_t decode_path;
+  int32_t decode_chunk;
+  int32_t prefill_kv_chunk;
+  int32_t reserved[5];
+} varlen_attn_options_t;
+
+varlen_status_t varlen_attn_fwd_ex(const void* q, const void* k, const void* v,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                   const int32_t* cu_seqlens_q_host,
+                                   const int32_t* cu_seqlens_kv_host, int32_t batch,
+                                   int64_t total_q, int64_t total_kv, int32_t num_heads,
+                                   int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                                   int32_t dtype, float scale, int32_t is_causal,
+                                   float softcap, void* out, void* stream,
+                                   const varlen_attn_options_t* options);
+
+/*
+ * varlen_attn_plan -- the host-side work scheduler on its own (no device
+ * work, no HIP call; usable without a GPU). It validates like
+ * varlen_attn_fwd (with host cu arrays) and fills `stats` with what a call
+ * with these arguments would launch. When `items` is non-NULL and
+ * `items_capacity` (in int32 elements) is large enough, it also writes the
+ * work items, VARLEN_PLAN_ITEM_INTS int32 each, kernel by kernel in launch
+ * order. Each item is:
+ *   { kind, seq, q_row_begin, q_rows, head_begin, heads, kv_begin, kv_end,
+ *     partial_base, n_splits, q_token0, kv_token0, L_q, L_kv, split, 0 }
+ * kind 0 = prefill (MFMA), 1 = prefill (fp32), 2 = split-KV decode,
+ * 3 = log-sum-exp combine. q_row_begin and kv_begin/kv_end are local to the
+ * sequence, q_token0/kv_token0 are cu_seqlens_q[seq]/cu_seqlens_kv[seq].
+ * partial_base is -1 when the item writes `out` directly; otherwise the
+ * item (split `split` of `n_splits`) writes fp32 partial rows starting at
+ * partial_base, and the combine item with the same partial_base merges the
+ * n_splits partials of every (row, head) into `out`.
+ * Returns VARLEN_OK or the validation status; VARLEN_ERR_INVALID_ARGUMENT if
+ * the item buffer is too small (stats are still filled).
+ */
+#define VARLEN_PLAN_ITEM_INTS 16
+typedef struct {
+  int64_t n_prefill_items;
+  int64_t n_decode_items;
+  int64_t n_combine_items;
+  int64_t n_partials;        /* fp32 partial rows (head x D+2 floats each) */
+  int64_t valid_pairs;       /* (query row, key) pairs the mask leaves visible */
+  int64_t visited_pairs;     /* pairs the scheduled tiles cover (>= valid_pairs) */
+  int64_t workspace_bytes;   /* device workspace the call needs */
+  int32_t waves_per_prefill_item;
+  int32_t heads_per_item;
+  int32_t reserved[6];
+} varlen_attn_plan_stats_t;
+
+varlen_status_t varlen_attn_plan(const int32_t* cu_seqlens_q_host,
+                                 const int32_t* cu_seqlens_kv_host, int32_t batch,
+                                 int64_t total_q, int64_t total_kv, int32_t num_heads,
+                                 int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                                 int32_t dtype, float scale, int32_t is_causal, float softcap,
+                                 const varlen_attn_options_t* options,
+                                 varlen_attn_plan_stats_t* stats, int32_t* items,
+                                 int64_t items_capacity);
+
+/*
+ * Number of (query row, key) pairs the mask leaves visible for host cu
+ * arrays ([PVA] "Causal alignment"): sum over sequences of L_q * L_kv, or
+ * with is_causal of sum_i clamp(i + L_kv - L_q + 1, 0, L_kv). Returns -1 on
+ * invalid arrays. The attention FLOPs of a call are 4 * pairs * Hq * D
+ * (QK^T and P.V, 2 flops per multiply-add, D == Dv).
+ */
+int64_t varlen_attn_valid_pairs(const int32_t* cu_seqlens_q_host,
+                                const int32_t* cu_seqlens_kv_host, int32_t batch,
+                                int32_t is_causal);
+
+/* Message of the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next call on this thread. */
+const char* varlen_attn_last_error(void);
+
+/* Frees the workspace of every device (after waiting for its last use).
+ * Safe to call at any time; the next call allocates again. */
+varlen_status_t varlen_attn_release(void);
+
+/* Library version as "major.minor.patch". */
+const char* varlen_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VARLEN_ATTN_H_ */

@@ -1,0 +1,245 @@
+"""Packed variable-length scaled-dot-product attention on MI355X (gfx950).
+
+A thin ctypes binding over ``libvarlen_attn.so`` (C ABI in
+``include/varlen_attn.h``). This module only marshals arguments: every step
+of the computation runs in the library's HIP kernels. There is no CPU or
+PyTorch fallback; if the library is missing, importing the binding's entry
+points raises.
+
+Semantics follow the packed op of the crate onnx-runtime-ep-cuda (page
+src/kernels/packed_varlen_attention.rs, module doc "Packed layout &
+cumulative offsets", "Schema (v1)", "Causal alignment"). Q is
+``[total_q, Hq, D]`` (or ``[total_q, Hq*D]``), K/V are ``[total_kv, Hkv, D]``
+(or rank 2), and int32 ``cu_seqlens`` arrays of length B+1 delimit the
+sequences.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "varlen_attn_fwd", "plan", "valid_pairs", "library_path", "load_library", "VarlenAttnError",
+    "PlanStats", "ITEM_INTS", "DTYPE_CODES",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libvarlen_attn.so")
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+ITEM_INTS = 16
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "BAD_SEQLENS", 3: "UNSUPPORTED", 4: "DEVICE",
+                5: "OUT_OF_MEMORY"}
+
+_lib = None
+
+
+class VarlenAttnError(RuntimeError):
+    """A non-OK status from the library; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{STATUS_NAMES.get(status, status)}] {message}")
+        self.status = status
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("decode_path", ctypes.c_int32), ("decode_chunk", ctypes.c_int32),
+                ("prefill_kv_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [("n_prefill_items", ctypes.c_int64), ("n_decode_items", ctypes.c_int64),
+                ("n_combine_items", ctypes.c_int64), ("n_partials", ctypes.c_int64),
+                ("valid_pairs", ctypes.c_int64), ("visited_pairs", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64), ("waves_per_prefill_item", ctypes.c_int32),
+                ("heads_per_item", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libvarlen_attn.so (built by ``python -m packed_varlen_scaled_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m packed_varlen_scaled_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    fwd_args = [vp, vp, vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, i32, f32, vp, vp]
+    lib.varlen_attn_fwd.argtypes = fwd_args
+    lib.varlen_attn_fwd.restype = ctypes.c_int
+    lib.varlen_attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Options)]
+    lib.varlen_attn_fwd_ex.restype = ctypes.c_int
+    lib.varlen_attn_plan.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, i32, f32,
+                                     ctypes.POINTER(Options), ctypes.POINTER(PlanStats), vp, i64]
+    lib.varlen_attn_plan.restype = ctypes.c_int
+    lib.varlen_attn_valid_pairs.argtypes = [vp, vp, i32, i32]
+    lib.varlen_attn_valid_pairs.restype = ctypes.c_int64
+    lib.varlen_attn_last_error.argtypes = []
+    lib.varlen_attn_last_error.restype = ctypes.c_char_p
+    lib.varlen_attn_release.argtypes = []
+    lib.varlen_attn_release.restype = ctypes.c_int
+    lib.varlen_attn_version.argtypes = []
+    lib.varlen_attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().varlen_attn_last_error().decode(errors="replace")
+        raise VarlenAttnError(status, msg)
+
+
+def _options(decode_path=0, decode_chunk=0, prefill_kv_chunk=0):
+    o = Options()
+    o.decode_path, o.decode_chunk, o.prefill_kv_chunk = int(decode_path), int(decode_chunk), int(prefill_kv_chunk)
+    return o
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"Q/K/V dtype {t.dtype} not supported (expected float32, float16 or bfloat16)")
+    return codes[t.dtype]
+
+
+def _resolve(t, heads: int, name: str):
+    """[tokens, heads, dim] or [tokens, heads*dim] -> (tokens, dim), like the op's
+    rank-2/rank-3 resolution (packed_varlen_attention.rs page, resolve_packed)."""
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() == 3:
+        if t.shape[1] != heads:
+            raise ValueError(f"{name} rank-3 head dim {t.shape[1]} must equal head count {heads}")
+        return t.shape[0], t.shape[2]
+    if t.dim() == 2:
+        if t.shape[1] % heads:
+            raise ValueError(f"{name} rank-2 hidden size {t.shape[1]} is not divisible by head count {heads}")
+        return t.shape[0], t.shape[1] // heads
+    raise ValueError(f"{name} must be rank 2 or 3, got rank {t.dim()}")
+
+
+def _host_cu(x):
+    import numpy as np
+    if x is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(x.cpu() if hasattr(x, "cpu") else x, dtype=np.int64))
+    if a.ndim != 1:
+        raise ValueError("cu_seqlens must be 1-D")
+    if a.size and (a.min() < -2**31 or a.max() >= 2**31):
+        raise ValueError("cu_seqlens values must fit int32")
+    return a.astype(np.int32)
+
+
+def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None,
+                    scale=None, is_causal: bool = False, softcap: float = 0.0, out=None,
+                    cu_seqlens_q_host=None, cu_seqlens_kv_host=None, stream=None,
+                    decode_path: int = 0, decode_chunk: int = 0, prefill_kv_chunk: int = 0):
+    """Packed varlen attention forward on the current GPU stream.
+
+    q, k, v: CUDA(HIP) tensors, rank 3 ``[T, H, D]`` or rank 2 ``[T, H*D]``.
+    cu_seqlens_q / cu_seqlens_kv: int32 CUDA tensors ``[B+1]``; the optional
+    host mirrors (any int sequence) spare the library a device->host read.
+    Returns ``out`` (allocated like q with v's head size when not given)."""
+    import torch
+    lib = load_library()
+    hq = int(num_heads)
+    hkv = int(kv_num_heads) if kv_num_heads else hq
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("Q, K, and V must use the same floating dtype")
+    if hq <= 0 or hkv <= 0:
+        raise ValueError("num_heads and kv_num_heads must be positive")
+    tq, d = _resolve(q, hq, "query")
+    tkv, dk = _resolve(k, hkv, "key")
+    tv, dv = _resolve(v, hkv, "value")
+    if dk != d:
+        raise ValueError(f"query head_size {d} != key head_size {dk}")
+    if tv != tkv:
+        raise ValueError(f"key token count {tkv} != value token count {tv}")
+    if out is None:
+        shape = (tq, hq, dv) if q.dim() == 3 else (tq, hq * dv)
+        out = torch.empty(shape, dtype=q.dtype, device=q.device)
+    elif out.dtype != q.dtype or not out.is_contiguous() or out.numel() != tq * hq * dv or not out.is_cuda:
+        raise ValueError("output must be a contiguous GPU tensor of the Q/K/V dtype with [total_q, num_heads, v_head_size] elements")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if cu is not None and (not cu.is_cuda or cu.dtype != torch.int32 or not cu.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if cu_seqlens_q is None and cu_seqlens_q_host is None:
+        raise ValueError("cu_seqlens_q is required")
+    n = (cu_seqlens_q.numel() if cu_seqlens_q is not None else len(cu_seqlens_q_host))
+    n_kv = (cu_seqlens_kv.numel() if cu_seqlens_kv is not None else len(cu_seqlens_kv_host))
+    if n != n_kv:
+        raise ValueError(f"cu_seqlens_q length {n} != cu_seqlens_kv length {n_kv} (both must be batch_size + 1)")
+    hq_host = _host_cu(cu_seqlens_q_host)
+    hkv_host = _host_cu(cu_seqlens_kv_host)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    opts = _options(decode_path, decode_chunk, prefill_kv_chunk)
+    with torch.cuda.device(q.device):
+        st = lib.varlen_attn_fwd_ex(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            cu_seqlens_q.data_ptr() if cu_seqlens_q is not None else None,
+            cu_seqlens_kv.data_ptr() if cu_seqlens_kv is not None else None,
+            hq_host.ctypes.data if hq_host is not None else None,
+            hkv_host.ctypes.data if hkv_host is not None else None,
+            n - 1, tq, tkv, hq, hkv, d, dv, code,
+            float(scale) if scale else 0.0, 1 if is_causal else 0, float(softcap),
+            out.data_ptr(), stream, ctypes.byref(opts))
+    _check(st)
+    return out
+
+
+def plan(cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None, head_dim: int = 128,
+         v_head_dim: int = 0, dtype: str = "bf16", scale: float = 0.0, is_causal: bool = False,
+         softcap: float = 0.0, with_items: bool = False, decode_path: int = 0, decode_chunk: int = 0,
+         prefill_kv_chunk: int = 0):
+    """Run the host scheduler alone (no GPU needed). Returns (stats dict, items or None);
+    items is an int32 array [n_items, 16] (see varlen_attn_plan in the header)."""
+    import numpy as np
+    lib = load_library()
+    cq, ckv = _host_cu(cu_seqlens_q), _host_cu(cu_seqlens_kv)
+    if cq.size != ckv.size:
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv lengths differ")
+    stats = PlanStats()
+    opts = _options(decode_path, decode_chunk, prefill_kv_chunk)
+    args = (cq.ctypes.data, ckv.ctypes.data, cq.size - 1, int(cq[-1]) if cq.size else 0,
+            int(ckv[-1]) if ckv.size else 0, int(num_heads), int(kv_num_heads or 0), int(head_dim),
+            int(v_head_dim), DTYPE_CODES[dtype], float(scale), 1 if is_causal else 0, float(softcap),
+            ctypes.byref(opts), ctypes.byref(stats))
+    _check(lib.varlen_attn_plan(*args, None, 0))
+    items = None
+    if with_items:
+        n = stats.n_prefill_items + stats.n_decode_items + stats.n_combine_items
+        items = np.zeros((max(n, 1), ITEM_INTS), dtype=np.int32)
+        _check(lib.varlen_attn_plan(*args, items.ctypes.data, items.size))
+        items = items[:n]
+    return stats.as_dict(), items
+
+
+def valid_pairs(cu_seqlens_q, cu_seqlens_kv, is_causal: bool) -> int:
+    """Visible (query row, key) pairs; attention FLOPs are 4 * pairs * Hq * D."""
+    lib = load_library()
+    cq, ckv = _host_cu(cu_seqlens_q), _host_cu(cu_seqlens_kv)
+    r = lib.varlen_attn_valid_pairs(cq.ctypes.data, ckv.ctypes.data, cq.size - 1, 1 if is_causal else 0)
+    if r < 0:
+        raise ValueError("invalid cu_seqlens arrays")
+    return int(r)
+
+
+def release():
+    """Free the library's per-device workspaces."""
+    _check(load_library().varlen_attn_release())
+
+
+def version() -> str:
+    return load_library().varlen_attn_version().decode()

@@ -1,0 +1,130 @@
+// Shared definitions of the gfx950 packed varlen attention kernels and their
+// host launcher: the work-item format the scheduler emits, the parameter block
+// every kernel receives, and small device helpers (MFMA operand types, type
+// conversion, cross-lane exchange).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pva {
+
+// One unit of scheduled work. Every field is a plain int32 so the host can
+// build the list without device help and the kernels read it with scalar
+// loads. Sequence-relative indices: q_row_begin, kv_begin, kv_end.
+struct WorkItem {
+  int32_t kind;          // ItemKind
+  int32_t seq;           // sequence b
+  int32_t q_row_begin;   // first query row of the tile (local to the sequence)
+  int32_t q_rows;        // rows in the tile
+  int32_t head_begin;    // first query head
+  int32_t heads;         // query heads (all in one kv group)
+  int32_t kv_begin;      // keys [kv_begin, kv_end) (local)
+  int32_t kv_end;
+  int32_t partial_base;  // -1: write out directly; else first fp32 partial row
+  int32_t n_splits;      // splits of this tile (combine: how many to merge)
+  int32_t q_token0;      // cu_seqlens_q[seq]
+  int32_t kv_token0;     // cu_seqlens_kv[seq]
+  int32_t len_q;         // L_q
+  int32_t len_kv;        // L_kv
+  int32_t split;         // index of this split in [0, n_splits)
+  int32_t pad;
+};
+static_assert(sizeof(WorkItem) == 64, "work item is 16 int32");
+
+enum ItemKind : int32_t {
+  kPrefillMfma = 0,
+  kPrefillF32 = 1,
+  kDecode = 2,
+  kCombine = 3,
+};
+
+enum DType : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Partial rows of split work: partial index of (split s, tile row r, head hh)
+// is partial_base + (s * q_rows + r) * heads + hh. part_o holds the split's
+// own normalised output (dv floats), part_lse its log2-sum-exp in the
+// kernels' log2 score units (-inf when the split saw no visible key).
+__host__ __device__ inline int64_t partial_index(const WorkItem& it, int split, int row, int hh) {
+  return (int64_t)it.partial_base + ((int64_t)split * it.q_rows + row) * it.heads + hh;
+}
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* part_o;
+  float* part_lse;
+  int32_t hq, hkv, group, d, dv;
+  int32_t causal;
+  int32_t softcap_on;
+  // Scores are worked in log2 units: y = s * score_log2 without softcap, and
+  // y = cap_log2 * tanh(s * scale / |softcap|) with it, where the tanh is
+  // formed as 1 - 2 / (exp2(s * tanh_log2) + 1).
+  float score_log2;  // scale * log2(e)
+  float cap_log2;    // |softcap| * log2(e)
+  float tanh_log2;   // 2 * scale / |softcap| * log2(e)
+  float scale;       // the effective scale (fp32 path)
+  float softcap;     // |softcap| (fp32 path)
+};
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float ninf() { return -__builtin_inff(); }
+
+// Two fp32 values -> two 16-bit values packed in one dword, round to nearest
+// even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 on gfx950).
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  f32x2_t x = {a, b};
+  if constexpr (BF16) {
+    bf16x2_t y = __builtin_convertvector(x, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, y);
+  } else {
+    f16x2_t y = __builtin_convertvector(x, f16x2_t);
+    return __builtin_bit_cast(uint32_t, y);
+  }
+}
+
+// 32x32x16 MFMA with fp32 accumulators on 8 packed 16-bit values per lane.
+template <bool BF16>
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+// 16x16x32 MFMA with fp32 accumulators on 8 packed 16-bit values per lane.
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float xor_lanes(float x, int mask) { return __shfl_xor(x, mask, 64); }
+#endif
+
+}  // namespace pva

@@ -1,0 +1,640 @@
+// Host side of the packed varlen attention library: argument validation, the
+// cu_seqlens-driven work scheduler, the per-device workspace, and the kernel
+// launches behind the C ABI declared in include/varlen_attn.h.
+//
+// Validation follows the packed op's execute() on the source page
+// src/kernels/packed_varlen_attention.rs (crate onnx-runtime-ep-cuda
+// 0.1.0-dev.6): dtype equality, kv heads dividing query heads, head sizes,
+// token counts, cumulative arrays that start at 0, never decrease and end at
+// the packed totals, and the output extent -- all before any device work.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/varlen_attn.h"
+#include "common.h"
+
+namespace pva {
+hipError_t launch_prefill_mfma(const Params& p, const WorkItem* items, int n, int dtype, int nw,
+                               hipStream_t s);
+hipError_t launch_decode(const Params& p, const WorkItem* items, int n, int dtype, hipStream_t s);
+hipError_t launch_combine(const Params& p, const WorkItem* items, int n, int dtype, hipStream_t s);
+hipError_t launch_prefill_f32(const Params& p, const WorkItem* items, int n, hipStream_t s);
+}  // namespace pva
+
+namespace {
+
+using pva::WorkItem;
+
+thread_local std::string g_last_error;
+
+varlen_status_t fail(varlen_status_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string("varlen_attn_fwd: ") + buf;
+  return code;
+}
+
+// ---------------------------------------------------------------------------
+// Arguments after defaults are resolved.
+// ---------------------------------------------------------------------------
+struct Problem {
+  int32_t batch;
+  int64_t total_q, total_kv;
+  int32_t hq, hkv, group, d, dv, dtype;
+  float scale;  // effective scale
+  int32_t causal;
+  float softcap;
+  const int32_t* cu_q;   // host
+  const int32_t* cu_kv;  // host
+};
+
+struct Options {
+  int32_t decode_path = 0;
+  int32_t decode_chunk = 0;
+  int32_t prefill_kv_chunk = 0;
+};
+
+Options resolve_options(const varlen_attn_options_t* o) {
+  Options r;
+  if (o) {
+    r.decode_path = o->decode_path;
+    r.decode_chunk = o->decode_chunk;
+    r.prefill_kv_chunk = o->prefill_kv_chunk;
+  }
+  return r;
+}
+
+// Scalar and shape checks that need no cu arrays.
+varlen_status_t check_scalars(int32_t batch, int64_t total_q, int64_t total_kv, int32_t num_heads,
+                              int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                              int32_t dtype, float scale, float softcap, Problem* pr) {
+  if (dtype != VARLEN_F32 && dtype != VARLEN_F16 && dtype != VARLEN_BF16)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "dtype code %d not supported (expected f32=0, f16=1 or bf16=2)", dtype);
+  if (num_heads <= 0)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "num_heads must be positive, got %d", num_heads);
+  const int32_t hkv = kv_num_heads <= 0 ? num_heads : kv_num_heads;
+  if (num_heads % hkv != 0)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT,
+                "num_heads %d must be a positive multiple of kv_num_heads %d (MHA/GQA/MQA)", num_heads, hkv);
+  if (head_dim <= 0) return fail(VARLEN_ERR_INVALID_ARGUMENT, "head_dim must be positive, got %d", head_dim);
+  const int32_t dv = v_head_dim <= 0 ? head_dim : v_head_dim;
+  if (batch < 1)
+    return fail(VARLEN_ERR_BAD_SEQLENS, "batch must be >= 1 (cu_seqlens of length batch + 1 >= 2), got %d", batch);
+  if (total_q < 0 || total_kv < 0 || total_q > INT32_MAX || total_kv > INT32_MAX)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "token totals must lie in [0, 2^31), got %lld and %lld",
+                (long long)total_q, (long long)total_kv);
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim)), got %g",
+                (double)scale);
+  if (!std::isfinite(softcap))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "softcap must be finite, got %g", (double)softcap);
+  pr->batch = batch;
+  pr->total_q = total_q;
+  pr->total_kv = total_kv;
+  pr->hq = num_heads;
+  pr->hkv = hkv;
+  pr->group = num_heads / hkv;
+  pr->d = head_dim;
+  pr->dv = dv;
+  pr->dtype = dtype;
+  pr->scale = scale == 0.f ? 1.0f / std::sqrt((float)head_dim) : scale;
+  pr->softcap = std::fabs(softcap);
+  return VARLEN_OK;
+}
+
+// The cumulative arrays: start at 0, never decrease, end at the packed total.
+varlen_status_t check_cu(const int32_t* cu, int32_t batch, int64_t total, const char* name) {
+  if (cu[0] != 0) return fail(VARLEN_ERR_BAD_SEQLENS, "%s[0] must be 0, got %d", name, cu[0]);
+  for (int32_t b = 0; b < batch; ++b) {
+    if (cu[b + 1] < cu[b])
+      return fail(VARLEN_ERR_BAD_SEQLENS, "%s must be non-decreasing, but element %d (%d) > %d (%d)", name, b,
+                  cu[b], b + 1, cu[b + 1]);
+  }
+  if ((int64_t)cu[batch] != total)
+    return fail(VARLEN_ERR_BAD_SEQLENS, "%s[%d] = %d must equal the packed token count %lld", name, batch,
+                cu[batch], (long long)total);
+  return VARLEN_OK;
+}
+
+varlen_status_t check_supported(const Problem& pr) {
+  if (pr.dtype == VARLEN_F32) {
+    if (pr.d > 128 || pr.dv > 128)
+      return fail(VARLEN_ERR_UNSUPPORTED, "f32 supports head_dim and v_head_dim <= 128, got %d and %d", pr.d, pr.dv);
+    return VARLEN_OK;
+  }
+  if (pr.d != pr.dv || (pr.d != 64 && pr.d != 128))
+    return fail(VARLEN_ERR_UNSUPPORTED, "f16/bf16 support head_dim == v_head_dim in {64, 128}, got %d and %d", pr.d,
+                pr.dv);
+  return VARLEN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The scheduler.
+// ---------------------------------------------------------------------------
+struct Plan {
+  std::vector<WorkItem> prefill;  // kind kPrefillMfma
+  std::vector<WorkItem> f32;      // kind kPrefillF32
+  std::vector<WorkItem> decode;   // kind kDecode
+  std::vector<WorkItem> combine;  // kind kCombine
+  int64_t n_partials = 0;
+  int64_t valid_pairs = 0;
+  int64_t visited_pairs_x_heads = 0;
+  int32_t prefill_waves = 0;
+  int32_t heads_per_item = 0;
+};
+
+int64_t valid_pairs_of(const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, bool causal) {
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t lq = (int64_t)cu_q[b + 1] - cu_q[b];
+    const int64_t lkv = (int64_t)cu_kv[b + 1] - cu_kv[b];
+    if (!causal) {
+      total += lq * lkv;
+      continue;
+    }
+    // row i sees clamp(i + off + 1, 0, lkv) keys, off = lkv - lq
+    const int64_t off = lkv - lq;
+    const int64_t i_first = std::max<int64_t>(0, -off);          // first row seeing >= 1 key
+    const int64_t i_full = std::max<int64_t>(0, lkv - off - 1);  // first row seeing all keys
+    const int64_t lo = std::min(lq, i_first);
+    const int64_t hi = std::min(lq, std::max(lo, i_full));
+    const int64_t n = hi - lo;  // rows seeing i + off + 1 keys
+    total += n * (off + 1) + (lo + hi - 1) * n / 2;
+    total += (lq - hi) * lkv;
+  }
+  return total;
+}
+
+WorkItem make_item(int32_t kind, int32_t b, const Problem& pr) {
+  WorkItem it;
+  std::memset(&it, 0, sizeof it);
+  it.kind = kind;
+  it.seq = b;
+  it.q_token0 = pr.cu_q[b];
+  it.kv_token0 = pr.cu_kv[b];
+  it.len_q = pr.cu_q[b + 1] - pr.cu_q[b];
+  it.len_kv = pr.cu_kv[b + 1] - pr.cu_kv[b];
+  it.partial_base = -1;
+  it.n_splits = 1;
+  it.split = 0;
+  return it;
+}
+
+// Keys [0, kv_end) that rows [r0, r0 + rows) of a sequence can see.
+int32_t visible_end(const WorkItem& it, int32_t r0, int32_t rows, bool causal) {
+  if (!causal) return it.len_kv;
+  const int64_t last = (int64_t)r0 + rows - 1;
+  const int64_t e = last + (it.len_kv - it.len_q) + 1;
+  return (int32_t)std::min<int64_t>(it.len_kv, std::max<int64_t>(0, e));
+}
+
+int largest_pow2_divisor_upto(int g, int cap) {
+  int r = 1;
+  for (int c = cap; c >= 1; c >>= 1) {
+    if (g % c == 0) {
+      r = c;
+      break;
+    }
+  }
+  return r;
+}
+
+// Splits tile items (all with the same rows and heads) over [kv_begin, kv_end)
+// in chunks; appends them (and their combine item) to `dst`/`plan.combine`.
+void emit_split(Plan& plan, std::vector<WorkItem>& dst, WorkItem base, int32_t kv_end, int32_t chunk) {
+  const int32_t n_splits = std::max<int32_t>(1, (kv_end + chunk - 1) / chunk);
+  if (n_splits == 1) {
+    base.kv_begin = 0;
+    base.kv_end = kv_end;
+    dst.push_back(base);
+    return;
+  }
+  base.partial_base = (int32_t)plan.n_partials;
+  base.n_splits = n_splits;
+  plan.n_partials += (int64_t)n_splits * base.q_rows * base.heads;
+  for (int32_t s = 0; s < n_splits; ++s) {
+    WorkItem it = base;
+    it.split = s;
+    it.kv_begin = s * chunk;
+    it.kv_end = std::min(kv_end, (s + 1) * chunk);
+    dst.push_back(it);
+  }
+  WorkItem c = base;
+  c.kind = pva::kCombine;
+  c.kv_begin = 0;
+  c.kv_end = kv_end;
+  plan.combine.push_back(c);
+}
+
+varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
+  const bool causal = pr.causal != 0;
+  plan.valid_pairs = valid_pairs_of(pr.cu_q, pr.cu_kv, pr.batch, causal);
+  if (pr.dtype == VARLEN_F32) {
+    plan.prefill_waves = 4;
+    plan.heads_per_item = 1;
+    for (int32_t b = 0; b < pr.batch; ++b) {
+      const WorkItem proto = make_item(pva::kPrefillF32, b, pr);
+      for (int32_t r0 = 0; r0 < proto.len_q; r0 += 32) {
+        const int32_t rows = std::min(32, proto.len_q - r0);
+        const int32_t kv_end = visible_end(proto, r0, rows, causal);
+        for (int32_t h = 0; h < pr.hq; ++h) {
+          WorkItem it = proto;
+          it.q_row_begin = r0;
+          it.q_rows = rows;
+          it.head_begin = h;
+          it.heads = 1;
+          it.kv_begin = 0;
+          it.kv_end = kv_end;
+          plan.f32.push_back(it);
+          plan.visited_pairs_x_heads += (int64_t)rows * kv_end;
+        }
+      }
+    }
+  } else {
+    // Prefill tiles: NH heads of one kv group x R blocks of 32 rows per item.
+    const int nh = largest_pow2_divisor_upto(pr.group, 8);
+    const int rblocks = nh >= 4 ? 1 : 4 / nh;
+    const int rows_per_item = 32 * rblocks;
+    plan.prefill_waves = nh * rblocks;
+    plan.heads_per_item = nh;
+    const int nh_dec = largest_pow2_divisor_upto(pr.group, 16);
+    const bool use_decode = opt.decode_path != 1;
+
+    // Split-KV decode chunk: aim for enough items to fill the chip several
+    // times over, in multiples of 128 keys.
+    int64_t decode_keys = 0;
+    for (int32_t b = 0; b < pr.batch; ++b) {
+      if (pr.cu_q[b + 1] - pr.cu_q[b] == 1) decode_keys += pr.cu_kv[b + 1] - pr.cu_kv[b];
+    }
+    int32_t dchunk = opt.decode_chunk;
+    if (dchunk <= 0) {
+      const int64_t groups = pr.hq / nh_dec;
+      const int64_t target_items = 2048;
+      int64_t c = (decode_keys * groups + target_items - 1) / target_items;
+      c = std::max<int64_t>(512, std::min<int64_t>(8192, c));
+      dchunk = (int32_t)c;
+    }
+    dchunk = (dchunk + 127) / 128 * 128;
+    const int32_t pchunk = opt.prefill_kv_chunk > 0 ? ((opt.prefill_kv_chunk + 63) / 64 * 64) : 0;
+
+    for (int32_t b = 0; b < pr.batch; ++b) {
+      const WorkItem proto = make_item(pva::kPrefillMfma, b, pr);
+      if (proto.len_q == 0) continue;
+      if (use_decode && proto.len_q == 1) {
+        for (int32_t h0 = 0; h0 < pr.hq; h0 += nh_dec) {
+          WorkItem it = proto;
+          it.kind = pva::kDecode;
+          it.q_row_begin = 0;
+          it.q_rows = 1;
+          it.head_begin = h0;
+          it.heads = nh_dec;
+          const int32_t kv_end = visible_end(proto, 0, 1, causal);
+          emit_split(plan, plan.decode, it, kv_end, dchunk);
+          plan.visited_pairs_x_heads += (int64_t)kv_end * nh_dec;
+        }
+        continue;
+      }
+      for (int32_t r0 = 0; r0 < proto.len_q; r0 += rows_per_item) {
+        const int32_t rows = std::min(rows_per_item, proto.len_q - r0);
+        const int32_t kv_end = visible_end(proto, r0, rows, causal);
+        for (int32_t h0 = 0; h0 < pr.hq; h0 += nh) {
+          WorkItem it = proto;
+          it.q_row_begin = r0;
+          it.q_rows = rows;
+          it.head_begin = h0;
+          it.heads = nh;
+          emit_split(plan, plan.prefill, it, kv_end, pchunk > 0 ? pchunk : std::max<int32_t>(kv_end, 1));
+          plan.visited_pairs_x_heads += (int64_t)rows * kv_end * nh;
+        }
+      }
+    }
+    // Longest first: the dispatcher hands out workgroups in index order, so
+    // this is the greedy longest-processing-time assignment over the CUs.
+    auto by_cost = [](const WorkItem& a, const WorkItem& b) {
+      const int64_t ca = (int64_t)(a.kv_end - a.kv_begin) * a.q_rows;
+      const int64_t cb = (int64_t)(b.kv_end - b.kv_begin) * b.q_rows;
+      return ca > cb;
+    };
+    std::stable_sort(plan.prefill.begin(), plan.prefill.end(), by_cost);
+    std::stable_sort(plan.decode.begin(), plan.decode.end(), by_cost);
+  }
+  return VARLEN_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  size_t items_off, lse_off, po_off, total;
+  size_t n_items;
+};
+
+Layout layout_of(const Plan& plan, int32_t dv) {
+  Layout l;
+  l.n_items = plan.prefill.size() + plan.f32.size() + plan.decode.size() + plan.combine.size();
+  l.items_off = 0;
+  l.lse_off = align_up(l.n_items * sizeof(WorkItem), 256);
+  l.po_off = align_up(l.lse_off + (size_t)plan.n_partials * sizeof(float), 256);
+  l.total = align_up(l.po_off + (size_t)plan.n_partials * (size_t)dv * sizeof(float), 256);
+  return l;
+}
+
+// ---------------------------------------------------------------------------
+// Per-device workspace.
+// ---------------------------------------------------------------------------
+struct DeviceState {
+  std::mutex mu;
+  void* dev = nullptr;
+  size_t dev_cap = 0;
+  void* host = nullptr;  // pinned staging of the work list
+  size_t host_cap = 0;
+  hipEvent_t copied = nullptr;  // after the last work-list upload
+  hipEvent_t done = nullptr;    // after the last call's kernels
+  bool pending = false;
+};
+
+constexpr int kMaxDevices = 64;
+DeviceState g_dev[kMaxDevices];
+
+varlen_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? VARLEN_ERR_OUT_OF_MEMORY : VARLEN_ERR_DEVICE, "%s failed: %s", what,
+              hipGetErrorString(e));
+}
+
+#define PVA_HIP(call, what)                        \
+  do {                                             \
+    hipError_t e_ = (call);                        \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                    const int32_t* cu_kv_dev, const int32_t* cu_q_host, const int32_t* cu_kv_host,
+                    int32_t batch, int64_t total_q, int64_t total_kv, int32_t num_heads,
+                    int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim, int32_t dtype,
+                    float scale, int32_t is_causal, float softcap, void* out, void* stream_v,
+                    const varlen_attn_options_t* options) {
+  g_last_error.clear();
+  Problem pr;
+  varlen_status_t st = check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim,
+                                     dtype, scale, softcap, &pr);
+  if (st != VARLEN_OK) return st;
+  pr.causal = is_causal != 0;
+  if (total_q > 0 && (!q || !out))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "query and output pointers must be non-null");
+  if (total_kv > 0 && (!k || !v))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "key and value pointers must be non-null");
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+  // The cu arrays on the host: the caller's mirrors, or a copy of the
+  // device arrays (the one synchronising case).
+  std::vector<int32_t> cuq_copy, cukv_copy;
+  if (!cu_q_host || !cu_kv_host) {
+    if (!cu_q_dev || !cu_kv_dev)
+      return fail(VARLEN_ERR_INVALID_ARGUMENT, "cu_seqlens_q/cu_seqlens_kv: need device arrays or host mirrors");
+    cuq_copy.resize(batch + 1);
+    cukv_copy.resize(batch + 1);
+    PVA_HIP(hipMemcpyAsync(cuq_copy.data(), cu_q_dev, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost, stream),
+            "reading cu_seqlens_q");
+    PVA_HIP(hipMemcpyAsync(cukv_copy.data(), cu_kv_dev, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost,
+                           stream),
+            "reading cu_seqlens_kv");
+    PVA_HIP(hipStreamSynchronize(stream), "synchronising after reading cu_seqlens");
+    cu_q_host = cuq_copy.data();
+    cu_kv_host = cukv_copy.data();
+  }
+  if ((st = check_cu(cu_q_host, batch, total_q, "cu_seqlens_q")) != VARLEN_OK) return st;
+  if ((st = check_cu(cu_kv_host, batch, total_kv, "cu_seqlens_kv")) != VARLEN_OK) return st;
+  if ((st = check_supported(pr)) != VARLEN_OK) return st;
+  pr.cu_q = cu_q_host;
+  pr.cu_kv = cu_kv_host;
+  if (total_q == 0) return VARLEN_OK;
+
+  Plan plan;
+  if ((st = build_plan(pr, resolve_options(options), plan)) != VARLEN_OK) return st;
+  const Layout lay = layout_of(plan, pr.dv);
+
+  int dev_id = 0;
+  PVA_HIP(hipGetDevice(&dev_id), "hipGetDevice");
+  if (dev_id < 0 || dev_id >= kMaxDevices) return fail(VARLEN_ERR_DEVICE, "device index %d out of range", dev_id);
+  DeviceState& ds = g_dev[dev_id];
+  std::lock_guard<std::mutex> lock(ds.mu);
+
+  if (!ds.copied) {
+    PVA_HIP(hipEventCreateWithFlags(&ds.copied, hipEventDisableTiming), "hipEventCreate");
+    PVA_HIP(hipEventCreateWithFlags(&ds.done, hipEventDisableTiming), "hipEventCreate");
+  }
+  // The previous call may still be reading the staging buffer (upload) or
+  // the device workspace (kernels on another stream).
+  if (ds.pending) {
+    PVA_HIP(hipEventSynchronize(ds.copied), "waiting for the previous work-list upload");
+    PVA_HIP(hipStreamWaitEvent(stream, ds.done, 0), "ordering after the previous call");
+  }
+  const size_t item_bytes = lay.n_items * sizeof(WorkItem);
+  if (lay.total > ds.dev_cap) {
+    if (ds.dev) {
+      PVA_HIP(hipEventSynchronize(ds.done), "waiting before growing the workspace");
+      PVA_HIP(hipFree(ds.dev), "hipFree");
+      ds.dev = nullptr;
+      ds.dev_cap = 0;
+    }
+    const size_t cap = std::max(lay.total, ds.dev_cap * 2);
+    PVA_HIP(hipMalloc(&ds.dev, cap), "allocating the workspace");
+    ds.dev_cap = cap;
+  }
+  if (item_bytes > ds.host_cap) {
+    if (ds.host) {
+      PVA_HIP(hipHostFree(ds.host), "hipHostFree");
+      ds.host = nullptr;
+      ds.host_cap = 0;
+    }
+    const size_t cap = std::max(item_bytes, ds.host_cap * 2);
+    PVA_HIP(hipHostMalloc(&ds.host, cap, hipHostMallocDefault), "allocating the pinned staging buffer");
+    ds.host_cap = cap;
+  }
+  WorkItem* stage = static_cast<WorkItem*>(ds.host);
+  size_t pos = 0;
+  const size_t off_prefill = pos;
+  std::memcpy(stage + pos, plan.prefill.data(), plan.prefill.size() * sizeof(WorkItem));
+  pos += plan.prefill.size();
+  const size_t off_decode = pos;
+  std::memcpy(stage + pos, plan.decode.data(), plan.decode.size() * sizeof(WorkItem));
+  pos += plan.decode.size();
+  const size_t off_f32 = pos;
+  std::memcpy(stage + pos, plan.f32.data(), plan.f32.size() * sizeof(WorkItem));
+  pos += plan.f32.size();
+  const size_t off_combine = pos;
+  std::memcpy(stage + pos, plan.combine.data(), plan.combine.size() * sizeof(WorkItem));
+  pos += plan.combine.size();
+
+  char* base = static_cast<char*>(ds.dev);
+  WorkItem* dev_items = reinterpret_cast<WorkItem*>(base + lay.items_off);
+  PVA_HIP(hipMemcpyAsync(dev_items, stage, item_bytes, hipMemcpyHostToDevice, stream), "uploading the work list");
+  PVA_HIP(hipEventRecord(ds.copied, stream), "hipEventRecord");
+  ds.pending = true;
+
+  pva::Params p;
+  std::memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.part_lse = reinterpret_cast<float*>(base + lay.lse_off);
+  p.part_o = reinterpret_cast<float*>(base + lay.po_off);
+  p.hq = pr.hq;
+  p.hkv = pr.hkv;
+  p.group = pr.group;
+  p.d = pr.d;
+  p.dv = pr.dv;
+  p.causal = pr.causal;
+  p.softcap_on = pr.softcap != 0.f;
+  const float log2e = 1.4426950408889634f;
+  p.scale = pr.scale;
+  p.softcap = pr.softcap;
+  p.score_log2 = pr.scale * log2e;
+  if (p.softcap_on) {
+    p.cap_log2 = pr.softcap * log2e;
+    p.tanh_log2 = 2.f * pr.scale / pr.softcap * log2e;
+  }
+
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess)
+    e = pva::launch_prefill_mfma(p, dev_items + off_prefill, (int)plan.prefill.size(), pr.dtype,
+                                 plan.prefill_waves, stream);
+  if (e == hipSuccess) e = pva::launch_decode(p, dev_items + off_decode, (int)plan.decode.size(), pr.dtype, stream);
+  if (e == hipSuccess) e = pva::launch_prefill_f32(p, dev_items + off_f32, (int)plan.f32.size(), stream);
+  if (e == hipSuccess)
+    e = pva::launch_combine(p, dev_items + off_combine, (int)plan.combine.size(), pr.dtype, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  PVA_HIP(hipEventRecord(ds.done, stream), "hipEventRecord");
+  return VARLEN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+varlen_status_t varlen_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_q_host,
+                                const int32_t* cu_seqlens_kv_host, int32_t batch, int64_t total_q,
+                                int64_t total_kv, int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                int32_t v_head_dim, int32_t dtype, float scale, int32_t is_causal,
+                                float softcap, void* out, void* stream) {
+  return run(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_host, cu_seqlens_kv_host, batch, total_q,
+             total_kv, num_heads, kv_num_heads, head_dim, v_head_dim, dtype, scale, is_causal, softcap, out, stream,
+             nullptr);
+}
+
+varlen_status_t varlen_attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_q_host,
+                                   const int32_t* cu_seqlens_kv_host, int32_t batch, int64_t total_q,
+                                   int64_t total_kv, int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                   int32_t v_head_dim, int32_t dtype, float scale, int32_t is_causal,
+                                   float softcap, void* out, void* stream, const varlen_attn_options_t* options) {
+  return run(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_host, cu_seqlens_kv_host, batch, total_q,
+             total_kv, num_heads, kv_num_heads, head_dim, v_head_dim, dtype, scale, is_causal, softcap, out, stream,
+             options);
+}
+
+varlen_status_t varlen_attn_plan(const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_kv_host,
+                                 int32_t batch, int64_t total_q, int64_t total_kv, int32_t num_heads,
+                                 int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim, int32_t dtype,
+                                 float scale, int32_t is_causal, float softcap,
+                                 const varlen_attn_options_t* options, varlen_attn_plan_stats_t* stats,
+                                 int32_t* items, int64_t items_capacity) {
+  g_last_error.clear();
+  if (stats) std::memset(stats, 0, sizeof *stats);
+  Problem pr;
+  varlen_status_t st = check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim,
+                                     dtype, scale, softcap, &pr);
+  if (st != VARLEN_OK) return st;
+  pr.causal = is_causal != 0;
+  if (!cu_seqlens_q_host || !cu_seqlens_kv_host)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "varlen_attn_plan needs host cu arrays");
+  if ((st = check_cu(cu_seqlens_q_host, batch, total_q, "cu_seqlens_q")) != VARLEN_OK) return st;
+  if ((st = check_cu(cu_seqlens_kv_host, batch, total_kv, "cu_seqlens_kv")) != VARLEN_OK) return st;
+  if ((st = check_supported(pr)) != VARLEN_OK) return st;
+  pr.cu_q = cu_seqlens_q_host;
+  pr.cu_kv = cu_seqlens_kv_host;
+  Plan plan;
+  if (total_q > 0) {
+    if ((st = build_plan(pr, resolve_options(options), plan)) != VARLEN_OK) return st;
+  } else {
+    plan.valid_pairs = 0;
+  }
+  const Layout lay = layout_of(plan, pr.dv);
+  if (stats) {
+    stats->n_prefill_items = (int64_t)(plan.prefill.size() + plan.f32.size());
+    stats->n_decode_items = (int64_t)plan.decode.size();
+    stats->n_combine_items = (int64_t)plan.combine.size();
+    stats->n_partials = plan.n_partials;
+    stats->valid_pairs = plan.valid_pairs;
+    stats->visited_pairs = plan.visited_pairs_x_heads / pr.hq;
+    stats->workspace_bytes = total_q > 0 ? (int64_t)lay.total : 0;
+    stats->waves_per_prefill_item = plan.prefill_waves;
+    stats->heads_per_item = plan.heads_per_item;
+  }
+  if (items) {
+    const int64_t need = (int64_t)lay.n_items * VARLEN_PLAN_ITEM_INTS;
+    if (items_capacity < need)
+      return fail(VARLEN_ERR_INVALID_ARGUMENT, "item buffer holds %lld int32, the plan needs %lld",
+                  (long long)items_capacity, (long long)need);
+    int32_t* dst = items;
+    for (const auto* vec : {&plan.prefill, &plan.decode, &plan.f32, &plan.combine}) {
+      std::memcpy(dst, vec->data(), vec->size() * sizeof(WorkItem));
+      dst += vec->size() * VARLEN_PLAN_ITEM_INTS;
+    }
+  }
+  return VARLEN_OK;
+}
+
+int64_t varlen_attn_valid_pairs(const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_kv_host,
+                                int32_t batch, int32_t is_causal) {
+  if (!cu_seqlens_q_host || !cu_seqlens_kv_host || batch < 1) return -1;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (cu_seqlens_q_host[b + 1] < cu_seqlens_q_host[b] || cu_seqlens_kv_host[b + 1] < cu_seqlens_kv_host[b])
+      return -1;
+  }
+  if (cu_seqlens_q_host[0] != 0 || cu_seqlens_kv_host[0] != 0) return -1;
+  return valid_pairs_of(cu_seqlens_q_host, cu_seqlens_kv_host, batch, is_causal != 0);
+}
+
+const char* varlen_attn_last_error(void) { return g_last_error.c_str(); }
+
+varlen_status_t varlen_attn_release(void) {
+  g_last_error.clear();
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) n = 0;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (int d = 0; d < kMaxDevices; ++d) {
+    DeviceState& ds = g_dev[d];
+    std::lock_guard<std::mutex> lock(ds.mu);
+    if (!ds.dev && !ds.host && !ds.copied) continue;
+    if (d < n) (void)hipSetDevice(d);
+    if (ds.done) (void)hipEventSynchronize(ds.done);
+    if (ds.dev) (void)hipFree(ds.dev);
+    if (ds.host) (void)hipHostFree(ds.host);
+    if (ds.copied) (void)hipEventDestroy(ds.copied);
+    if (ds.done) (void)hipEventDestroy(ds.done);
+    ds.dev = ds.host = nullptr;
+    ds.dev_cap = ds.host_cap = 0;
+    ds.copied = ds.done = nullptr;
+    ds.pending = false;
+  }
+  if (n > 0) (void)hipSetDevice(cur);
+  return VARLEN_OK;
+}
+
+const char* varlen_attn_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes compare every output element; the full-size workloads compare
+sampled rows (the oracle computes them one by one on a sub-batch of the
+sampled sequences). Every case prints what it runs before it runs it.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from parity import compare, gather_gpu, oracle_all, oracle_sampled, run_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _workload(dtype="bf16", hq=8, hkv=2, d=128, causal=True, softcap=0.0, scale=0.0, sigma=1.0, seed=11):
+    return synth.Workload("custom", 0, hq, hkv, d, dtype, causal, softcap, scale, sigma, seed)
+
+
+def _batch(w, lq, lkv):
+    return synth.make_batch(w, lq, lkv, device="cuda")
+
+
+SMALL = [
+    # (name, workload kwargs, lq, lkv)
+    ("bf16_gqa4_causal", dict(hq=8, hkv=2), [70, 1, 129, 33, 0, 200], [70, 1, 129, 33, 5, 200]),
+    ("bf16_gqa4_tail_aligned", dict(hq=8, hkv=2), [40, 3, 100, 1], [300, 90, 100, 17]),
+    ("bf16_lq_gt_lkv", dict(hq=4, hkv=1), [50, 65], [10, 64]),
+    ("bf16_noncausal_mha", dict(hq=4, hkv=4, causal=False), [77, 128, 5], [31, 128, 200]),
+    ("bf16_gqa8_softcap", dict(hq=16, hkv=2, softcap=30.0, sigma=1.5), [150, 64, 1], [150, 64, 900]),
+    ("bf16_mqa", dict(hq=6, hkv=1), [90, 2], [90, 70]),
+    ("bf16_gqa16", dict(hq=32, hkv=2), [45, 1], [45, 600]),
+    ("bf16_d64", dict(hq=8, hkv=2, d=64), [100, 1, 37], [100, 513, 37]),
+    ("f16_gqa4_causal", dict(dtype="f16", hq=8, hkv=2), [70, 1, 129], [70, 700, 129]),
+    ("f16_d64_softcap", dict(dtype="f16", hq=4, hkv=2, d=64, softcap=5.0), [33, 1], [60, 300]),
+    ("bf16_scale", dict(hq=4, hkv=2, scale=0.3, causal=False), [64, 20], [64, 96]),
+    ("bf16_negative_softcap", dict(hq=4, hkv=2, softcap=-8.0), [80], [80]),
+    ("f32_gqa_causal", dict(dtype="f32", hq=8, hkv=2, d=64), [70, 1, 33], [70, 200, 40]),
+    ("f32_d128_softcap", dict(dtype="f32", hq=4, hkv=4, d=128, softcap=5.0, causal=False), [40, 3], [17, 90]),
+    ("f32_odd_dim", dict(dtype="f32", hq=2, hkv=1, d=40, causal=True), [9, 30], [12, 30]),
+]
+
+
+@pytest.mark.parametrize("name,kw,lq,lkv", SMALL, ids=[s[0] for s in SMALL])
+def test_small_shapes_match_oracle(name, kw, lq, lkv):
+    w = _workload(**kw)
+    _say(name, w, lq, lkv)
+    batch = _batch(w, lq, lkv)
+    got = run_gpu(batch).double().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv)
+    want = oracle_all(batch)
+    ma, rel = compare(got, want, w.dtype)
+    _say(name, "max_abs", ma, "rel_l2", rel)
+
+
+@pytest.mark.parametrize("opts", [dict(decode_path=1), dict(decode_chunk=128), dict(prefill_kv_chunk=64),
+                                  dict(prefill_kv_chunk=192, decode_chunk=256)])
+def test_split_paths_match_oracle(opts):
+    w = _workload(hq=16, hkv=2, softcap=20.0)
+    lq, lkv = [1, 100, 1, 257, 1], [1000, 700, 129, 300, 5]
+    _say("split paths", opts, lq, lkv)
+    batch = _batch(w, lq, lkv)
+    got = run_gpu(batch, **opts).double().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv)
+    compare(got, oracle_all(batch), w.dtype)
+
+
+def test_fully_masked_and_empty_rows_are_exactly_zero():
+    w = _workload(hq=8, hkv=2)
+    lq, lkv = [70, 5, 40, 1], [3, 0, 0, 0]
+    _say("masked rows", lq, lkv)
+    batch = _batch(w, lq, lkv)
+    got = run_gpu(batch).float().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv)
+    # sequence 0: L_q=70, L_kv=3, offset -67: rows 0..66 see nothing
+    assert np.all(got[:67] == 0) and np.any(got[67:70] != 0)
+    assert np.all(got[70:] == 0)  # sequences without keys
+
+
+def test_single_key_returns_value_row():
+    import torch
+    w = _workload(hq=8, hkv=2, causal=False, softcap=3.0)
+    lq, lkv = [5, 1, 40], [1, 1, 1]
+    batch = _batch(w, lq, lkv)
+    got = run_gpu(batch).view(batch.total_q, 8, 128)
+    seq = np.repeat(np.arange(3), lq)
+    for t in range(batch.total_q):
+        for h in range(8):
+            assert torch.equal(got[t, h], batch.v[seq[t], h // 4])
+
+
+def test_gqa_exact_head_mapping_on_gpu():
+    import torch
+    w = _workload(hq=8, hkv=2, causal=False)
+    batch = _batch(w, [40, 1], [70, 300])
+    batch.k[:] = 1.0  # identical keys: output = mean of V of the head's kv group
+    for g in range(2):
+        batch.v[:, g, :] = g + 1
+    got = run_gpu(batch).view(batch.total_q, 8, 128).float()
+    for h in range(8):
+        assert torch.all(got[:, h] == h // 4 + 1)
+
+
+def test_neighbour_sequence_cannot_leak():
+    """Poisoning the next sequence's K/V with inf/nan must not change a single
+    bit of the previous sequence's output (block-diagonal attention; key tiles
+    past a sequence end are zero-filled, never just masked)."""
+    import torch
+    w = _workload(hq=8, hkv=2)
+    lq, lkv = [77, 1, 50], [77, 130, 50]
+    batch = _batch(w, lq, lkv)
+    a = run_gpu(batch).clone()
+    k0 = int(batch.cu_kv[1])
+    batch.k[k0:] = float("inf")
+    batch.v[k0:] = float("nan")
+    b = run_gpu(batch)
+    assert torch.equal(a[:77], b[:77])
+
+
+def test_rerun_is_bitwise_deterministic():
+    import torch
+    w = _workload(hq=16, hkv=2, softcap=10.0)
+    batch = _batch(w, [300, 1, 129], [300, 5000, 200])
+    outs = [run_gpu(batch).clone() for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_sequence_alone_equals_sequence_in_batch():
+    """Prefill tiles start at each sequence's own row 0, so a sequence gives
+    the same bits alone as inside a batch."""
+    import torch
+    w = _workload(hq=8, hkv=2)
+    lq = [100, 257, 64]
+    full = _batch(w, lq, lq)
+    a = run_gpu(full)
+    q0, q1 = int(full.cu_q[1]), int(full.cu_q[2])
+    alone = synth.Batch(w, [257], [257], synth.cu_seqlens([257]), synth.cu_seqlens([257]),
+                        full.q[q0:q1].contiguous(), full.k[q0:q1].contiguous(), full.v[q0:q1].contiguous())
+    b = run_gpu(alone)
+    assert torch.equal(a[q0:q1], b)
+
+
+def test_rank2_layout_and_device_cu_read():
+    """Rank-2 [T, H*D] tensors and cu arrays read from the device (no host
+    mirrors) give the same result as rank-3 with host mirrors."""
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = _workload(hq=8, hkv=2)
+    batch = _batch(w, [30, 1, 90], [60, 100, 90])
+    a = run_gpu(batch)
+    cu_q = torch.from_numpy(batch.cu_q).cuda()
+    cu_kv = torch.from_numpy(batch.cu_kv).cuda()
+    b = pva.varlen_attn_fwd(batch.q.view(batch.total_q, -1), batch.k.view(batch.total_kv, -1),
+                            batch.v.view(batch.total_kv, -1), cu_q, cu_kv, 8, 2, is_causal=True)
+    torch.cuda.synchronize()
+    assert b.shape == (batch.total_q, 8 * 128)
+    assert torch.equal(a.view(batch.total_q, -1), b)
+
+
+def test_tiny_fp32_workload_full():
+    batch = synth.workload_batch("tiny_fp32", device="cuda")
+    _say("tiny_fp32", batch.lq)
+    got = run_gpu(batch).double().cpu().numpy().reshape(batch.total_q, 4, 64)
+    ma, _ = compare(got, oracle_all(batch), "f32")
+    _say("tiny_fp32 max_abs", ma)
+
+
+# Reduced versions of the four large workloads (same heads, types, masks and
+# value scales; a handful of sequences the oracle finishes in seconds).
+REDUCED = {
+    "ragged_causal_prefill": ([233, 1000, 130], None),
+    "long_causal_softcap": ([700, 1500], None),
+    "chunked_prefill_cache": ([3, 100, 512, 1], [3 + 2000, 100, 512 + 800, 1 + 8192]),
+    "packed_decode": ([1] * 6, [256, 300, 4097, 1000, 32768, 777]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REDUCED))
+def test_reduced_workloads_full_compare(name):
+    w = synth.WORKLOADS[name]
+    lq, lkv = REDUCED[name]
+    lkv = lkv or lq
+    _say("reduced", name, lq, lkv)
+    batch = synth.make_batch(w, lq, lkv, device="cuda")
+    got = run_gpu(batch).double().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv)
+    ma, rel = compare(got, oracle_all(batch), w.dtype)
+    _say("reduced", name, "max_abs", ma, "rel_l2", rel)
+
+
+@pytest.mark.parametrize("name", ["ragged_causal_prefill", "long_causal_softcap", "chunked_prefill_cache",
+                                  "packed_decode"])
+def test_full_size_workloads_sampled(name):
+    """Full-size batch, launched exactly as the benchmark launches it; the
+    oracle checks sampled rows of a few sequences (including the longest)."""
+    import torch
+    w = synth.WORKLOADS[name]
+    _say("full", name)
+    batch = synth.workload_batch(name, device="cuda")
+    out = run_gpu(batch)
+    longest = int(np.argmax(np.asarray(batch.lkv)))
+    seqs = sorted({0, longest, len(batch.lq) - 1, len(batch.lq) // 2})
+    picks = sample_rows(batch, seqs, rows_per_seq=6 if name != "packed_decode" else 1)
+    want = oracle_sampled(batch, picks)
+    got = gather_gpu(batch, out, picks)
+    ma, rel = compare(got, want, w.dtype)
+    _say("full", name, len(picks), "rows max_abs", ma, "rel_l2", rel)
+    assert torch.isfinite(out.float()).all()
+    del batch, out
+    torch.cuda.empty_cache()

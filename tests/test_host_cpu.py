@@ -1,0 +1,221 @@
+"""Host-side logic of the C-ABI library, run without a GPU.
+
+* the library loads and exports every function include/varlen_attn.h declares;
+* argument / cu_seqlens validation returns the documented status before any
+  device work (the packed op's execute() rules on the page
+  src/kernels/packed_varlen_attention.rs);
+* the scheduler covers every visible (row, key) pair of every head exactly
+  once, writes every output row exactly once, and never schedules a tile that
+  lies wholly above the causal frontier;
+* the valid-pair count matches a brute-force count of the tail-aligned mask.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import packed_varlen_scaled_amd as pva
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "varlen_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(varlen_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pva.load_library()
+    names = _declared_functions()
+    assert "varlen_attn_fwd" in names and len(names) >= 6
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+    assert pva.version().count(".") == 2
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+def _fwd_status(cu_q, cu_kv, hq=4, hkv=2, d=64, dv=0, dtype=2, scale=0.0, causal=0, softcap=0.0,
+                total_q=None, total_kv=None, batch=None, ptr=1):
+    """Call varlen_attn_fwd with host mirrors and dummy (never dereferenced)
+    device pointers: every case here must fail validation first."""
+    lib = pva.load_library()
+    cq = np.ascontiguousarray(cu_q, dtype=np.int32)
+    ck = np.ascontiguousarray(cu_kv, dtype=np.int32)
+    b = len(cq) - 1 if batch is None else batch
+    tq = int(cq[-1]) if total_q is None else total_q
+    tk = int(ck[-1]) if total_kv is None else total_kv
+    fake = ctypes.c_void_p(ptr) if ptr else None
+    st = lib.varlen_attn_fwd(fake, fake, fake, None, None, cq.ctypes.data, ck.ctypes.data, b, tq, tk,
+                             hq, hkv, d, dv, dtype, scale, causal, softcap, fake, None)
+    return st, lib.varlen_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,fragment", [
+    (dict(hq=8, hkv=3), 1, "multiple of kv_num_heads"),
+    (dict(hq=0), 1, "num_heads must be positive"),
+    (dict(d=0), 1, "head_dim must be positive"),
+    (dict(dtype=7), 1, "dtype code"),
+    (dict(scale=-1.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(softcap=float("inf")), 1, "softcap"),
+    (dict(batch=0), 2, "batch must be >= 1"),
+    (dict(total_q=11), 2, "must equal the packed token count"),
+    (dict(d=96), 3, "f16/bf16 support head_dim"),
+    (dict(d=128, dv=64), 3, "f16/bf16 support head_dim"),
+    (dict(dtype=0, d=256), 3, "f32 supports"),
+    (dict(ptr=0), 1, "must be non-null"),
+])
+def test_validation_rejects_before_any_device_work(kwargs, status, fragment):
+    st, msg = _fwd_status(_cu([3, 4]), _cu([5, 2]), **kwargs)
+    assert st == status, msg
+    assert msg.startswith("varlen_attn_fwd: ") and fragment in msg, msg
+
+
+@pytest.mark.parametrize("cu_q,cu_kv,fragment", [
+    ([1, 3, 7], [0, 5, 7], "cu_seqlens_q[0] must be 0"),
+    ([0, 5, 4], [0, 5, 7], "non-decreasing"),
+    ([0, 3, 7], [0, 6, 5], "non-decreasing"),
+])
+def test_bad_cu_seqlens(cu_q, cu_kv, fragment):
+    st, msg = _fwd_status(np.array(cu_q), np.array(cu_kv), total_q=cu_q[-1] if cu_q[-1] > 0 else 7)
+    assert st == 2 and fragment in msg, msg
+
+
+def test_empty_query_batch_is_ok_without_device_work():
+    st, msg = _fwd_status(_cu([0, 0]), _cu([3, 0]))
+    assert st == 0, msg
+
+
+# --------------------------------------------------------------------------
+# Valid-pair count.
+# --------------------------------------------------------------------------
+def _brute_pairs(lq, lkv, causal):
+    n = 0
+    for a, b in zip(lq, lkv):
+        for i in range(a):
+            for j in range(b):
+                if not causal or j <= i + b - a:
+                    n += 1
+    return n
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_valid_pairs_matches_brute_force(causal):
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        bsz = int(rng.integers(1, 6))
+        lq = rng.integers(0, 40, size=bsz).tolist()
+        lkv = rng.integers(0, 40, size=bsz).tolist()
+        assert pva.valid_pairs(_cu(lq), _cu(lkv), causal) == _brute_pairs(lq, lkv, causal)
+
+
+# --------------------------------------------------------------------------
+# Scheduler coverage.
+# --------------------------------------------------------------------------
+KIND_PREFILL, KIND_F32, KIND_DECODE, KIND_COMBINE = 0, 1, 2, 3
+
+
+def _coverage(lq, lkv, hq, hkv, causal, dtype="bf16", d=128, **opts):
+    stats, items = pva.plan(_cu(lq), _cu(lkv), hq, hkv, head_dim=d, dtype=dtype, is_causal=causal,
+                            with_items=True, **opts)
+    cq, ck = _cu(lq), _cu(lkv)
+    # visits[(token, head)] -> list of key index arrays
+    visits = {}
+    writes = {}
+    combined = {}
+    for it in items:
+        kind, seq, r0, rows, h0, nh, kv0, kv1, pbase, nsplit, qt0, kt0, Lq, Lkv, split, _ = it.tolist()
+        assert qt0 == cq[seq] and kt0 == ck[seq] and Lq == lq[seq] and Lkv == lkv[seq]
+        assert 0 <= r0 and r0 + rows <= Lq and 0 <= kv0 <= kv1 <= Lkv
+        assert h0 % nh == 0 and (h0 // (hq // hkv)) == ((h0 + nh - 1) // (hq // hkv)), "item spans kv groups"
+        for r in range(r0, r0 + rows):
+            for h in range(h0, h0 + nh):
+                key = (qt0 + r, h)
+                if kind == KIND_COMBINE:
+                    combined[key] = combined.get(key, 0) + 1
+                    continue
+                visits.setdefault(key, []).append(np.arange(kv0, kv1))
+                if pbase < 0:
+                    writes[key] = writes.get(key, 0) + 1
+    for b in range(len(lq)):
+        off = lkv[b] - lq[b]
+        for i in range(lq[b]):
+            for h in range(hq):
+                key = (cq[b] + i, h)
+                got = np.concatenate(visits.get(key, [np.zeros(0, int)]))
+                # every visible key visited exactly once
+                visible = np.arange(lkv[b]) if not causal else np.arange(max(0, min(lkv[b], i + off + 1)))
+                cnt = np.bincount(got, minlength=max(lkv[b], 1)) if got.size else np.zeros(max(lkv[b], 1), int)
+                assert np.all(cnt[visible] == 1), (b, i, h)
+                assert cnt.sum() - cnt[visible].sum() >= 0
+                # each output row written exactly once, directly or by one combine
+                assert writes.get(key, 0) + combined.get(key, 0) == 1, (b, i, h)
+    return stats, items
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (32, 8), (64, 8), (6, 2), (16, 1)])
+def test_scheduler_covers_each_visible_pair_once(causal, hq, hkv):
+    lq = [1, 33, 70, 0, 5, 129, 1]
+    lkv = [7, 33, 150, 4, 0, 100, 0]
+    stats, _ = _coverage(lq, lkv, hq, hkv, causal)
+    assert stats["valid_pairs"] == _brute_pairs(lq, lkv, causal)
+    assert stats["visited_pairs"] >= stats["valid_pairs"]
+
+
+@pytest.mark.parametrize("opts", [dict(decode_path=1), dict(decode_chunk=128), dict(prefill_kv_chunk=64),
+                                  dict(prefill_kv_chunk=100, decode_chunk=300)])
+def test_scheduler_split_options_keep_coverage(opts):
+    lq = [1, 40, 200, 1, 3]
+    lkv = [700, 300, 200, 65, 1000]
+    stats, items = _coverage(lq, lkv, 32, 8, True, **opts)
+    if opts.get("decode_path") == 1:
+        assert stats["n_decode_items"] == 0
+    if opts.get("prefill_kv_chunk") or opts.get("decode_chunk"):
+        assert stats["n_combine_items"] > 0 and stats["n_partials"] > 0
+
+
+def test_scheduler_f32_items():
+    stats, items = _coverage([5, 17, 32, 64], [5, 17, 32, 64], 4, 4, False, dtype="f32", d=64)
+    assert set(items[:, 0].tolist()) == {KIND_F32}
+    assert stats["n_decode_items"] == 0
+
+
+def test_causal_tiles_never_start_above_the_frontier():
+    lq, lkv = [300, 64], [300, 500]
+    _, items = pva.plan(_cu(lq), _cu(lkv), 32, 8, is_causal=True, with_items=True)
+    for it in items:
+        kind, seq, r0, rows, *_ = it.tolist()
+        kv1, Lq, Lkv = it[7], it[12], it[13]
+        last = r0 + rows - 1
+        assert kv1 == min(Lkv, last + Lkv - Lq + 1)
+
+
+def test_longest_items_first():
+    lq = [2048, 130, 900]
+    _, items = pva.plan(_cu(lq), _cu(lq), 32, 8, is_causal=True, with_items=True)
+    pre = items[items[:, 0] == KIND_PREFILL]
+    cost = (pre[:, 7] - pre[:, 6]) * pre[:, 3]
+    assert np.all(np.diff(cost) <= 0)
+
+
+def test_workload_plans_fit():
+    """The five workload shapes plan without error and report sane sizes."""
+    import synth
+    for name, w in synth.WORKLOADS.items():
+        lq, lkv = synth.draw_lengths(name)
+        stats, _ = pva.plan(_cu(lq), _cu(lkv), w.num_heads, w.kv_num_heads, head_dim=w.head_dim,
+                            dtype=w.dtype, is_causal=w.is_causal, softcap=w.softcap)
+        assert stats["valid_pairs"] > 0
+        assert stats["workspace_bytes"] < 512 << 20
+        if name == "packed_decode":
+            assert stats["n_decode_items"] >= 1024
