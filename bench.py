@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed varlen attention hot path on one MI355X.
+
+A step is one varlen_attn_fwd call over the full synthetic batch of a
+workload (argument validation, work scheduling, work-list upload and every
+kernel), with Q/K/V already resident in HBM. The default workload is the
+ragged causal prefill (B=16, L ~ U{128..2048}, Hq=32, Hkv=8, D=128, bf16).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line. ``value`` is valid-pair TFLOP/s (4 * pairs * Hq * D per
+step / step time) for prefill workloads and HBM GB/s (Q+K+V+O bytes per step
+/ step time) for the decode workload. ``roofline`` reports the dominant
+kernel: its algorithmic work per launch over its average duration, timed with
+HIP events recorded by the library on the launch stream over the timed
+region. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
+same batch (rank 0, N=1).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "varlen attn TFLOP/s (valid pairs) + % bf16 MFMA peak; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DEFAULT_WORKLOAD = "ragged_causal_prefill"
+KERNEL_SOURCES = {
+    "prefill_mfma": ["packed_varlen_scaled_amd/csrc/prefill_mfma.hip", "packed_varlen_scaled_amd/csrc/common.h"],
+    "decode": ["packed_varlen_scaled_amd/csrc/decode.hip", "packed_varlen_scaled_amd/csrc/common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def row_keys(lq, lkv, causal):
+    """Visible keys of every query row, sequence by sequence (measurement only)."""
+    out = []
+    for a, b in zip(lq, lkv):
+        i = np.arange(a, dtype=np.int64)
+        out.append(np.clip(i + (b - a) + 1, 0, b) if causal else np.full(a, b, dtype=np.int64))
+    return out
+
+
+def source_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kind: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, or None when
+    the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_sha(kind):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def sub_batch(batch, seqs):
+    """Host copies of the chosen sequences as their own packed batch."""
+    import torch
+    import synth
+    qs, ks, vs, lq, lkv = [], [], [], [], []
+    for b in seqs:
+        q0, q1 = int(batch.cu_q[b]), int(batch.cu_q[b + 1])
+        k0, k1 = int(batch.cu_kv[b]), int(batch.cu_kv[b + 1])
+        qs.append(batch.q[q0:q1].cpu())
+        ks.append(batch.k[k0:k1].cpu())
+        vs.append(batch.v[k0:k1].cpu())
+        lq.append(q1 - q0)
+        lkv.append(k1 - k0)
+    return torch.cat(qs), torch.cat(ks), torch.cat(vs), synth.cu_seqlens(lq), synth.cu_seqlens(lkv), lq, lkv
+
+
+def cpu_baseline(batch, decode: bool, budget_s: float = 12.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the batch."""
+    import oracle
+    w = batch.workload
+    threads = min(16, os.cpu_count() or 1)
+    rng = np.random.default_rng(0)
+    if decode:
+        # whole sequences (every head), growing the sample until the budget is used
+        order = rng.permutation(len(batch.lq)).tolist()
+        seqs, t_used, bytes_done, n_rows = [], 0.0, 0, 0
+        while order and t_used < budget_s:
+            take = [order.pop() for _ in range(min(4, len(order)))]
+            q, k, v, cq, ckv, lq, lkv = sub_batch(batch, take)
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, cq, ckv, w.num_heads, w.kv_num_heads, scale=w.scale or None,
+                             is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, threads=threads)
+            t_used += time.perf_counter() - t0
+            el = 2 if w.dtype != "f32" else 4
+            bytes_done += (q.numel() * 2 + k.numel() + v.numel()) * el
+            seqs += take
+            n_rows += sum(lq) * w.num_heads
+        return {"value": bytes_done / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": f"{len(seqs)} of {len(batch.lq)} sequences, all {w.num_heads} heads "
+                          f"({n_rows} rows), {t_used:.1f} s"}
+    # prefill: random (token, head) rows of a few sequences, sized to the budget
+    keys = row_keys(batch.lq, batch.lkv, w.is_causal)
+    seqs = sorted(set(rng.choice(len(batch.lq), size=min(4, len(batch.lq)), replace=False).tolist()))
+    q, k, v, cq, ckv, lq, lkv = sub_batch(batch, seqs)
+    sub_keys = np.concatenate([keys[b] for b in seqs])
+    n_all = int(cq[-1]) * w.num_heads
+    perm = rng.permutation(n_all)
+    flops_per_row = 4.0 * sub_keys[perm // w.num_heads] * w.head_dim
+    # calibrate on a growing slice (until it takes >= 1 s or covers every row),
+    # then run a slice sized to the budget
+    n_cal = min(n_all, 64)
+    while True:
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, cq, ckv, w.num_heads, w.kv_num_heads, scale=w.scale or None,
+                         is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, rows=perm[:n_cal],
+                         threads=threads)
+        t_cal = max(time.perf_counter() - t0, 1e-6)
+        if t_cal >= 1.0 or n_cal >= n_all:
+            break
+        n_cal = min(n_all, n_cal * 4)
+    rate = flops_per_row[:n_cal].sum() / t_cal
+    cum = np.cumsum(flops_per_row)
+    n = int(min(n_all, max(n_cal, np.searchsorted(cum, rate * budget_s))))
+    reps = 1
+    if n == n_all:  # a small workload: time whole passes over it until the budget is used
+        reps = max(1, int(budget_s / max(t_cal * flops_per_row.sum() / flops_per_row[:n_cal].sum(), 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.attention(q, k, v, cq, ckv, w.num_heads, w.kv_num_heads, scale=w.scale or None,
+                         is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, rows=perm[:n], threads=threads)
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": float(flops_per_row[:n].sum() / dt / 1e12), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} random (token, head) rows of sequences {seqs} "
+                      f"({int(flops_per_row[:n].sum() / 4 / w.head_dim)} valid pairs), "
+                      f"{reps} pass(es), {dt * reps:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes, 5 times (the known-size "
+                         "reference that HBM byte counters are calibrated against), then exit")
+    a = ap.parse_args(argv)
+    if a.copy_reference:
+        import torch
+        n = a.copy_reference << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes": n, "copies": 5}), flush=True)
+        return 0
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the hot path is a single-GPU kernel set and this build "
+              "launches no multi-GPU work (see DESIGN.md for how it would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import packed_varlen_scaled_amd as pva
+    import synth
+
+    if a.workload not in synth.WORKLOADS:
+        print(f"unknown workload {a.workload}; choose from {sorted(synth.WORKLOADS)}", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pva.load_library()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[a.workload]
+    decode = a.workload == "packed_decode"
+    log(f"[bench] generating {a.workload} on cuda:0")
+    batch = synth.workload_batch(a.workload, device="cuda:0")
+    cu_q = torch.from_numpy(batch.cu_q).cuda()
+    cu_kv = torch.from_numpy(batch.cu_kv).cuda()
+    out = torch.empty(batch.total_q, w.num_heads, w.dv, dtype=batch.q.dtype, device="cuda:0")
+    pairs = pva.valid_pairs(batch.cu_q, batch.cu_kv, w.is_causal)
+    flops = 4.0 * pairs * w.num_heads * w.head_dim
+    el = 4 if w.dtype == "f32" else 2
+    io_bytes = (batch.q.numel() + batch.k.numel() + batch.v.numel() + out.numel()) * el
+    stats, _ = pva.plan(batch.cu_q, batch.cu_kv, w.num_heads, w.kv_num_heads, head_dim=w.head_dim,
+                        dtype=w.dtype, is_causal=w.is_causal, softcap=w.softcap)
+    log(f"[bench] total_q={batch.total_q} total_kv={batch.total_kv} valid_pairs={pairs} plan={stats}")
+
+    def step():
+        pva.varlen_attn_fwd(batch.q, batch.k, batch.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads,
+                            scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap, out=out,
+                            cu_seqlens_q_host=batch.cu_q, cu_seqlens_kv_host=batch.cu_kv)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps")
+    pva.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    host_s = 0.0
+    for _ in range(a.steps):
+        h0 = time.perf_counter()
+        step()
+        host_s += time.perf_counter() - h0
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = pva.profile_read()
+    pva.profile_enable(False)
+    ms = elapsed / a.steps * 1e3
+    log(f"[bench] {ms:.4f} ms/step; host call {host_s / a.steps * 1e3:.4f} ms/step; kernels {prof}")
+
+    if decode:
+        value, unit = io_bytes / (ms / 1e3) / 1e9, "GB/s"
+        kind = "decode"
+        k_ms, k_n, _ = prof[kind]
+        avg = k_ms / max(k_n, 1)
+        achieved = io_bytes / (avg / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        value, unit = flops / (ms / 1e3) / 1e12, "TFLOP/s"
+        kind = "prefill_mfma" if w.dtype != "f32" else "prefill_f32"
+        k_ms, k_n, _ = prof[kind]
+        avg = k_ms / max(k_n, 1)
+        achieved = flops / (avg / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    traffic = load_traffic(kind, a.workload) if kind in KERNEL_SOURCES else None
+    roof["traffic"] = traffic
+    roof["kernel"] = kind
+    roof["kernel_avg_ms"] = avg
+    roof["launches"] = k_n
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(batch, decode, a.cpu_budget)
+        log(f"[bench] cpu_baseline {cpu}")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": a.workload, "batch": w.batch, "num_heads": w.num_heads,
+                   "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,
+                   "softcap": w.softcap, "total_q": batch.total_q, "total_kv": batch.total_kv,
+                   "valid_pairs": pairs, "flops_per_step": flops, "io_bytes_per_step": io_bytes,
+                   "pct_of_peak": 100.0 * (value / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS)),
+                   "host_ms_per_call": host_s / a.steps * 1e3,
+                   "kernel_ms_per_step": {k: v[0] / max(a.steps, 1) for k, v in prof.items() if v[1]},
+                   "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

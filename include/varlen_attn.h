@@ -208,6 +208,25 @@ int64_t varlen_attn_valid_pairs(const int32_t* cu_seqlens_q_host,
                                 const int32_t* cu_seqlens_kv_host, int32_t batch,
                                 int32_t is_causal);
 
+/*
+ * Kernel timing for measurement tools (not needed for computing). While
+ * enabled, every call records a pair of HIP events on its stream around each
+ * kernel it launches. varlen_attn_profile_read waits for the recorded events,
+ * adds their elapsed times to per-kernel totals and returns the totals since
+ * the last enable. Index k of the arrays: 0 prefill (MFMA), 1 prefill
+ * (fp32), 2 split-KV decode, 3 combine, 4 work-list upload.
+ * varlen_attn_profile_enable(0) stops recording; (1) clears and starts.
+ */
+#define VARLEN_PROFILE_KINDS 5
+typedef struct {
+  double total_ms[VARLEN_PROFILE_KINDS];
+  int64_t launches[VARLEN_PROFILE_KINDS];
+  int64_t items[VARLEN_PROFILE_KINDS];  /* workgroups launched (upload: bytes) */
+} varlen_attn_profile_t;
+
+varlen_status_t varlen_attn_profile_enable(int32_t enable);
+varlen_status_t varlen_attn_profile_read(varlen_attn_profile_t* out);
+
 /* Message of the last failed call on this thread ("" if none). The pointer
  * stays valid until the next call on this thread. */
 const char* varlen_attn_last_error(void);

@@ -57,6 +57,14 @@ class PlanStats(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
 
 
+class ProfileTotals(ctypes.Structure):
+    _fields_ = [("total_ms", ctypes.c_double * 5), ("launches", ctypes.c_int64 * 5),
+                ("items", ctypes.c_int64 * 5)]
+
+
+PROFILE_KINDS = ("prefill_mfma", "prefill_f32", "decode", "combine", "upload")
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -84,6 +92,10 @@ def load_library():
     lib.varlen_attn_last_error.restype = ctypes.c_char_p
     lib.varlen_attn_release.argtypes = []
     lib.varlen_attn_release.restype = ctypes.c_int
+    lib.varlen_attn_profile_enable.argtypes = [i32]
+    lib.varlen_attn_profile_enable.restype = ctypes.c_int
+    lib.varlen_attn_profile_read.argtypes = [ctypes.POINTER(ProfileTotals)]
+    lib.varlen_attn_profile_read.restype = ctypes.c_int
     lib.varlen_attn_version.argtypes = []
     lib.varlen_attn_version.restype = ctypes.c_char_p
     _lib = lib
@@ -234,6 +246,18 @@ def valid_pairs(cu_seqlens_q, cu_seqlens_kv, is_causal: bool) -> int:
     if r < 0:
         raise ValueError("invalid cu_seqlens arrays")
     return int(r)
+
+
+def profile_enable(on: bool = True):
+    """Start (clearing totals) or stop recording HIP events around each kernel."""
+    _check(load_library().varlen_attn_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """Per-kernel totals since the last enable: {kind: (total_ms, launches, items)}."""
+    t = ProfileTotals()
+    _check(load_library().varlen_attn_profile_read(ctypes.byref(t)))
+    return {k: (t.total_ms[i], t.launches[i], t.items[i]) for i, k in enumerate(PROFILE_KINDS)}
 
 
 def release():

@@ -125,6 +125,53 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float xor_lanes(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// The value of lane l ^ 32 (v_permlane32_swap exchanges the two wave halves;
+// each lane keeps its own value in one result and receives its partner's in
+// the other).
+__device__ __forceinline__ float partner32(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
+}
+
+// max / sum of a lane's value and its partner's (lane l ^ 32); both lanes of
+// a pair get bit-identical results.
+__device__ __forceinline__ float max_with_partner32(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float sum_with_partner32(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// Sum of the two 16-bit values packed in w, in fp32 (v_dot2 against 1.0).
+template <bool BF16>
+__device__ __forceinline__ float sum2(uint32_t w, float acc) {
+  if constexpr (BF16) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+  } else {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, w), one, acc, false);
+  }
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i receives element i % 4 of the 4-element rows addressed by
+// lanes 4j + i/4, j = 0..3: when lanes 4j..4j+3 address consecutive
+// 4-element pieces of row j of a [rows][cols] 16-bit array, lane i gets
+// column i of rows 0..3.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
 #endif
 
 }  // namespace pva

@@ -13,36 +13,72 @@
 // Work item: one sequence, up to 32*R consecutive query rows, NH query heads
 // of one kv head (NH * R waves of 64 lanes), keys [kv_begin, kv_end).
 // Each wave owns one query head and 32 query rows. Per key tile of 64 keys:
-//   * the workgroup stages K as [key][d] and V transposed as [d][key] in LDS,
-//     once for all NH heads of the group (the GQA reuse);
+//   * the workgroup streams K and V from HBM straight into LDS (global_load_lds,
+//     no staging registers), both as [key][d] with 16-byte chunks permuted
+//     by key so that neither the K fragment reads nor the V transpose reads
+//     collide in LDS banks,
+//     double-buffered, once for all NH heads of the group (the GQA reuse);
+//     one barrier per tile;
 //   * S^T = K . Q^T on 32x32x16 MFMA: lane l then holds 32 scores of query
-//     row l%32, so the row max / sum need one exchange between lane halves;
-//   * online softmax in registers in log2 units (exp2 with log2(e) folded
-//     into the scale);
-//   * O^T += V^T . P^T on 32x32x16 MFMA, P rounded to the I/O type, with the
-//     score accumulator registers reused directly as the B operand (the MFMA
-//     reduction order over keys is free, so V^T is read in the order the
-//     score layout leaves the keys in).
+//     row l%32, so a row's max / sum need one exchange between lane halves
+//     (v_permlane32_swap);
+//   * softmax in registers in log2 units (exp2 with log2(e) folded into the
+//     scale). Each row's first tile fixes a reference max and every later P
+//     is taken against it, so O is never rescaled inside the loop (P stays
+//     below 2^TAU, which bf16 / f16 and the fp32 accumulators hold); a
+//     workgroup whose scores climb past that bound redoes its item with the
+//     textbook running-max softmax. Either way the result is the same
+//     softmax up to rounding;
+//   * O^T += V^T . P^T on 32x32x16 MFMA, P rounded to the I/O type with the
+//     score accumulator registers reused directly as the B operand (the
+//     MFMA reduction order over keys is free, so V^T is read in the order
+//     the score layout leaves the keys in), V^T fragments gathered from the
+//     [key][d] tile with the LDS transpose read; the row sum l is taken from
+//     the same rounded P (v_dot2), so numerator and denominator agree.
 // Rows of the tile that lie past the sequence are never stored; keys at or
 // past kv_end are zero-filled in LDS (so data of the next sequence can never
 // reach a product) and masked.
+#include <type_traits>
+
 #include "common.h"
 
 namespace pva {
 
-template <int D, bool BF16, int NW, bool SOFTCAP>
-__global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(Params p,
-                                                               const WorkItem* __restrict__ items) {
-  constexpr int BN = 64;              // keys per tile
-  constexpr int KS = D + 8;           // LDS K row stride (16-bit elements)
-  constexpr int VS = BN + 4;          // LDS V^T row stride
-  constexpr int NT = NW * 64;
-  constexpr int DCH = D / 8;          // 16-byte chunks per key row
-  constexpr int CHUNKS = BN * DCH;    // chunks per K (or V) tile
-  constexpr int CPT = (CHUNKS + NT - 1) / NT;
+enum TileMode : int { kFirst = 0, kPlain = 1, kMasked = 2, kSafe = 3 };
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+// LDS chunk swizzle: 16-byte chunk c of key row r is stored at chunk
+// c ^ chunk_perm<D>(r). gfx950's LDS serves 64 banks of 4 bytes per clock, so
+// a 128-dim bf16 row (256 bytes) spans the banks exactly once and a 64-dim row
+// half of them. The permutation makes both access patterns of the kernel
+// conflict-free: 16 consecutive rows at one logical chunk (the K fragment
+// reads) and 4 consecutive rows x 4 consecutive chunks (the transpose reads
+// of V).
+template <int D>
+__device__ __forceinline__ int chunk_perm(int r) {
+  if constexpr (D == 128) {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  } else {
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+}
+
+template <int D, bool BF16, int NW, bool SOFTCAP>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
+  constexpr int BN = 64;                   // keys per tile
+  constexpr int DCH = D / 8;               // 16-byte chunks per key row
+  constexpr int TILE = BN * D;             // 16-bit elements per K (or V) tile
+  constexpr int ROWS_PER_BLOCK = 512 / D;  // key rows per 1 KB wave load
+  constexpr int BLOCKS = BN / ROWS_PER_BLOCK;
+  constexpr int BPW = BLOCKS / NW;         // 1 KB blocks per wave per tile (K and V each)
+  static_assert(BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
+  // Largest exponent P may take above 1 without a rescale: bf16 shares fp32's
+  // exponent range; f16 tops out near 2^16.
+  constexpr float TAU = BF16 ? 20.0f : 15.0f;
+
+  // K0 K1 V0 V1, each [key][d] with 16-byte chunk c of row r stored at chunk
+  // c ^ chunk_perm<D>(r).
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];
 
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
@@ -80,89 +116,131 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(Params p,
   f32x16_t oacc[D / 32];
 #pragma unroll
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
-  float m_run = ninf();
-  float l_run = 0.f;
+  float m_ref = ninf();  // reference max of the row (log2 units)
+  float l_run = 0.f;     // this lane's half of the row sum
+  bool overflow = false;
 
-  const int64_t tok_stride = (int64_t)p.hkv * D;
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + ((int64_t)it.kv_token0 * p.hkv + g) * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + ((int64_t)it.kv_token0 * p.hkv + g) * D;
+  // ---- HBM -> LDS tile loads ------------------------------------------------
+  // Wave w fills 1 KB blocks w, w + NW, ... of each tile; lane L of a block
+  // lands at byte 16*L of it, i.e. row L / DCH of the block, stored chunk
+  // L % DCH, so it fetches logical chunk (L % DCH) ^ chunk_perm<D>(row).
+  const int64_t tok_stride = (int64_t)p.hkv * D;  // elements between consecutive tokens
+  const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.k) +
+                                                    ((int64_t)it.kv_token0 * p.hkv + g) * D);
+  const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) +
+                                                    ((int64_t)it.kv_token0 * p.hkv + g) * D);
+  const int blk_row = wave * ROWS_PER_BLOCK + lane / DCH;  // row in the first block of this wave
+  const int dma_chunk = (lane % DCH) ^ chunk_perm<D>(blk_row);  // same for every block of the wave
+  const uint32_t dma_off = (uint32_t)((blk_row * tok_stride + dma_chunk * 8) * 2);
+  const uint32_t dma_step = (uint32_t)(NW * ROWS_PER_BLOCK * tok_stride * 2);  // bytes between this wave's blocks
 
-  u32x4_t kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int kt) {
+  auto issue_tile = [&](int kt, int buf) {
+    const char* kb = kbase + (int64_t)kt * tok_stride * 2;
+    const char* vb = vbase + (int64_t)kt * tok_stride * 2;
+    uint16_t* kl = lds + buf * TILE + wave * 512;
+    uint16_t* vl = lds + (2 + buf) * TILE + wave * 512;
+    const int rows = kv_end - kt;
+    if (rows >= BN) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + c * NT;
-      const int key = chunk / DCH;
-      const int d0 = (chunk % DCH) * 8;
-      const int j = kt + key;
-      const bool ok = (CHUNKS % NT == 0 || chunk < CHUNKS) && j < kv_end;
-      const u32x4_t zero = {0u, 0u, 0u, 0u};
-      kreg[c] = ok ? *reinterpret_cast<const u32x4_t*>(kbase + j * tok_stride + d0) : zero;
-      vreg[c] = ok ? *reinterpret_cast<const u32x4_t*>(vbase + j * tok_stride + d0) : zero;
-    }
-  };
-  auto store_tile = [&]() {
+      for (int i = 0; i < BPW; ++i) {
+        __builtin_amdgcn_global_load_lds(kb + dma_off + i * dma_step, kl + i * NW * 512, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + dma_off + i * dma_step, vl + i * NW * 512, 16, 0, 0);
+      }
+    } else {
+      // last tile: rows at or past kv_end are zeros (never the next sequence)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = tid + c * NT;
-      if (CHUNKS % NT != 0 && chunk >= CHUNKS) continue;
-      const int key = chunk / DCH;
-      const int d0 = (chunk % DCH) * 8;
-      *reinterpret_cast<u32x4_t*>(&ks[key * KS + d0]) = kreg[c];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = vreg[c][e];
-        vt[(d0 + 2 * e) * VS + key] = (uint16_t)(w & 0xffffu);
-        vt[(d0 + 2 * e + 1) * VS + key] = (uint16_t)(w >> 16);
+      for (int i = 0; i < BPW; ++i) {
+        const int r = blk_row + i * NW * ROWS_PER_BLOCK;
+        if (r < rows) {
+          __builtin_amdgcn_global_load_lds(kb + dma_off + i * dma_step, kl + i * NW * 512, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vb + dma_off + i * dma_step, vl + i * NW * 512, 16, 0, 0);
+        } else {
+          const u32x4_t zero = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4_t*>(kl + i * NW * 512 + 8 * lane) = zero;
+          *reinterpret_cast<u32x4_t*>(vl + i * NW * 512 + 8 * lane) = zero;
+        }
       }
     }
   };
 
-  if (kv_begin < kv_end) load_tile(kv_begin);
-  for (int kt = kv_begin; kt < kv_end; kt += BN) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + BN < kv_end) load_tile(kt + BN);
-    // Whole tile beyond every row of this wave (causal), or no rows at all.
-    if (!wave_active || (p.causal && kt > wave_last + off)) continue;
-    const bool need_mask = (kt + BN > kv_end) || (p.causal && kt + BN - 1 > wave_first + off);
+  // ---- per-lane LDS read addresses (element offsets in buffer 0) -------------
+  // K fragment of S^T: key row 32*mt + l32, logical chunk 2*kk + half.
+  int k_addr[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) k_addr[kk] = l32 * D + (((2 * kk + half) ^ chunk_perm<D>(l32)) << 3);
+  // V^T fragments via the transpose read: 16-lane group G covers head dims
+  // 16*(G%2) + 0..15 of keys 4*(G/2) + 0..3 (+8) of each 16-key block.
+  const int trg = lane >> 4;
+  const int tr_i = lane & 15;
+  const int tr_key = 4 * (trg >> 1) + (tr_i >> 2);
+  int v_addr[D / 32], v_addr8[D / 32];  // rows tr_key and tr_key + 8 of each 16-key block
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) {
+    const int dd = 32 * mb + 16 * (trg & 1) + 4 * (tr_i & 3);
+    v_addr[mb] = tr_key * D + (((dd >> 3) ^ chunk_perm<D>(tr_key)) << 3) + (dd & 7);
+    v_addr8[mb] = (tr_key + 8) * D + (((dd >> 3) ^ chunk_perm<D>(tr_key + 8)) << 3) + (dd & 7);
+  }
+
+  // One key tile. MODE selects the masking and the softmax bookkeeping:
+  //   kFirst  - first tile of the item: masked; sets each row's reference
+  //             max m_ref, against which every later P is taken;
+  //   kPlain  - a tile that needs no mask for any row of the workgroup;
+  //   kMasked - a tile that crosses the causal frontier or kv_end;
+  //   kSafe   - the textbook online softmax (masked, running max, O rescaled
+  //             on every tile), used only to redo an item whose scores rose
+  //             more than 2^TAU above the first tile's.
+  // Outside kSafe, P = 2^(y - m_ref) stays below 2^TAU: bf16 and fp32 have
+  // the range for that, and O is never rescaled inside the loop.
+  auto compute = [&](int buf, int kt, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool MASK = MODE != kPlain;
+    const uint16_t* ks = lds + buf * TILE;
+    const uint16_t* vs = lds + (2 + buf) * TILE;
 
     // ---- S^T = K Q^T -------------------------------------------------------
+    // K fragments stream through a ring of KPF register slots, KPF - 1 steps
+    // ahead of the MFMAs that use them, so LDS latency hides behind MFMA work.
+    constexpr int KPF = 4;
+    constexpr int KSTEPS = D / 16;
     f32x16_t sacc[BN / 32];
 #pragma unroll
     for (int mt = 0; mt < BN / 32; ++mt) sacc[mt] = f32x16_t{};
+    u32x4_t kfr[KPF][BN / 32];
+    auto load_k = [&](int kk) {
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+      for (int mt = 0; mt < BN / 32; ++mt)
+        kfr[kk % KPF][mt] = *reinterpret_cast<const u32x4_t*>(ks + k_addr[kk] + 32 * mt * D);
+    };
 #pragma unroll
-      for (int mt = 0; mt < BN / 32; ++mt) {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t*>(&ks[(32 * mt + l32) * KS + 16 * kk + 8 * half]);
-        sacc[mt] = mfma32<BF16>(a, qf[kk], sacc[mt]);
-      }
+    for (int kk = 0; kk < KPF - 1 && kk < KSTEPS; ++kk) load_k(kk);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kk + KPF - 1 < KSTEPS) load_k(kk + KPF - 1);
+#pragma unroll
+      for (int mt = 0; mt < BN / 32; ++mt) sacc[mt] = mfma32<BF16>(kfr[kk % KPF][mt], qf[kk], sacc[mt]);
     }
     // sacc[mt][r] is the score of query row l32 and key
     // kt + 32*mt + 8*(r/4) + 4*half + r%4.
 
     // ---- mask and tile max ---------------------------------------------------
+    if constexpr (MASK) {
+#pragma unroll
+      for (int mt = 0; mt < BN / 32; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool bad = key >= kv_end || (p.causal && key > i_local + off);
+          sacc[mt][r] = bad ? ninf() : sacc[mt][r];
+        }
+      }
+    }
     float mx = ninf();
 #pragma unroll
     for (int mt = 0; mt < BN / 32; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = sacc[mt][r];
-        if (need_mask) {
-          const int key = kt + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool bad = key >= kv_end || (p.causal && key > i_local + off);
-          s = bad ? ninf() : s;
-          sacc[mt][r] = s;
-        }
-        mx = fmaxf(mx, s);
-      }
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sacc[mt][r]), sacc[mt][r + 1]);
     }
-    mx = fmaxf(mx, xor_lanes(mx, 32));
-
-    // ---- online softmax (log2 units) ------------------------------------
+    mx = max_with_partner32(mx);
     float tmax;
     if constexpr (SOFTCAP) {
       tmax = (mx == ninf()) ? ninf()
@@ -170,10 +248,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(Params p,
     } else {
       tmax = mx * p.score_log2;
     }
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == ninf()) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    float psum = 0.f;
+    if constexpr (MODE == kFirst) {
+      m_ref = tmax;
+    } else if constexpr (MODE == kSafe) {
+      const float m_new = fmaxf(m_ref, tmax);
+      const float alpha = (m_new == ninf()) ? 1.f : exp2_fast(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+    } else {
+      overflow = overflow || (tmax > m_ref + TAU);
+    }
+    const float m_use = (m_ref == ninf()) ? 0.f : m_ref;
+
+    // ---- P = 2^(y - m_use) -----------------------------------------------------
 #pragma unroll
     for (int mt = 0; mt < BN / 32; ++mt) {
 #pragma unroll
@@ -184,23 +273,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(Params p,
           const float t = exp2_fast(s * p.tanh_log2);
           const float rr = rcp_fast(t + 1.f);
           pr = exp2_fast(__builtin_fmaf(rr, -2.f * p.cap_log2, p.cap_log2 - m_use));
-          if (need_mask) pr = (s == ninf()) ? 0.f : pr;
+          if constexpr (MASK) pr = (s == ninf()) ? 0.f : pr;
         } else {
           pr = exp2_fast(__builtin_fmaf(s, p.score_log2, -m_use));
         }
         sacc[mt][r] = pr;
-        psum += pr;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
 
-    // ---- P (B operand) -------------------------------------------------------
+    // ---- P (B operand) and its row sum ----------------------------------------
     // Key block kb (16 keys) takes registers 8*(kb%2) .. +7 of sacc[kb/2]:
     // lane half h holds keys 16kb + 4h + 0..3 and 16kb + 8 + 4h + 0..3.
     u32x4_t pf[BN / 16];
+    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < BN / 16; ++kb) {
       const int mt = kb >> 1;
@@ -209,27 +294,92 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(Params p,
                        pack2<BF16>(sacc[mt][b0 + 2], sacc[mt][b0 + 3]),
                        pack2<BF16>(sacc[mt][b0 + 4], sacc[mt][b0 + 5]),
                        pack2<BF16>(sacc[mt][b0 + 6], sacc[mt][b0 + 7])};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) psum = sum2<BF16>(pf[kb][e], psum);
     }
+    l_run += psum;
 
     // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
     for (int kb = 0; kb < BN / 16; ++kb) {
+      u32x4_t a[D / 32];
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
-        const uint16_t* src = &vt[(32 * mb + l32) * VS + 16 * kb + 4 * half];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 8);
-        const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
-        oacc[mb] = mfma32<BF16>(a, pf[kb], oacc[mb]);
+        const u32x2_t lo = lds_read_tr16(vs + v_addr[mb] + 16 * kb * D);
+        const u32x2_t hi = lds_read_tr16(vs + v_addr8[mb] + 16 * kb * D);
+        a[mb] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      }
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32<BF16>(a[mb], pf[kb], oacc[mb]);
+    }
+  };
+
+  // ---- key-tile loops ----------------------------------------------------------
+  // Every loop step: wait for this wave's loads of the current tile, one
+  // barrier (all waves' loads landed; the other buffer is free again), start
+  // streaming the next tile into the other buffer, compute the current one.
+  const int n_tiles = (kv_end - kv_begin + BN - 1) / BN;
+  // Tiles [1, n_plain) need no mask for any row of the workgroup: they end at
+  // or before kv_end and before the first row's causal frontier.
+  int n_plain = n_tiles;
+  {
+    const int lim_end = (kv_end - kv_begin) / BN;  // full tiles
+    n_plain = min(n_plain, lim_end);
+    if (p.causal) {
+      const int frontier = it.q_row_begin + off + 1;  // keys [0, frontier) seen by every row
+      n_plain = min(n_plain, max(0, (frontier - kv_begin) / BN));
+    }
+    n_plain = max(n_plain, 1);
+  }
+  auto step = [&](int t) {
+    const int kt = kv_begin + t * BN;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(kt + BN, (t + 1) & 1);
+    return kt;
+  };
+  auto run_pass = [&](auto safe_tag) {
+    constexpr bool SAFE = decltype(safe_tag)::value;
+    if (n_tiles > 0) issue_tile(kv_begin, 0);
+    if constexpr (SAFE) {
+      for (int t = 0; t < n_tiles; ++t) {
+        const int kt = step(t);
+        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kSafe>{});
+      }
+    } else {
+      if (n_tiles > 0) {
+        const int kt = step(0);
+        compute(0, kt, std::integral_constant<int, kFirst>{});
+      }
+      for (int t = 1; t < n_plain; ++t) {
+        const int kt = step(t);
+        compute(t & 1, kt, std::integral_constant<int, kPlain>{});
+      }
+      for (int t = max(n_plain, 1); t < n_tiles; ++t) {
+        const int kt = step(t);
+        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
       }
     }
+  };
+
+  run_pass(std::false_type{});
+  // Redo the item with the rescaling softmax if any row's scores rose more
+  // than 2^TAU above its first tile's (decided for the whole workgroup: the
+  // tiles are loaded by all of its waves).
+  __syncthreads();
+  if (__syncthreads_or(__any(overflow && row_ok) ? 1 : 0)) {
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
+    m_ref = ninf();
+    l_run = 0.f;
+    run_pass(std::true_type{});
   }
 
   if (!wave_active || !row_ok) return;
   // oacc[mb][r] is the output of row l32 at head dim 32*mb + 8*(r/4) + 4*half + r%4.
-  const float l_tot = l_run + xor_lanes(l_run, 32);
+  const float l_tot = sum_with_partner32(l_run);
+  const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
   if (it.partial_base < 0) {
-    const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     uint16_t* dst = static_cast<uint16_t*>(p.out) + (tok * p.hq + head) * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb) {
@@ -242,7 +392,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(Params p,
       }
     }
   } else {
-    const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     const int64_t pidx = partial_index(it, it.split, my_row, hh);
     float* po = p.part_o + pidx * D;
 #pragma unroll
@@ -255,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_mfma_kernel(Params p,
         *reinterpret_cast<f32x4_t*>(po + d) = w;
       }
     }
-    if (half == 0) p.part_lse[pidx] = (l_tot == 0.f) ? ninf() : m_run + log2_fast(l_tot);
+    if (half == 0) p.part_lse[pidx] = (l_tot == 0.f) ? ninf() : m_ref + log2_fast(l_tot);
   }
 }
 

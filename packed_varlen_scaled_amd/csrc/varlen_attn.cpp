@@ -366,6 +366,60 @@ struct DeviceState {
 constexpr int kMaxDevices = 64;
 DeviceState g_dev[kMaxDevices];
 
+// ---------------------------------------------------------------------------
+// Optional kernel timing (HIP events around each launch, on its stream).
+// ---------------------------------------------------------------------------
+struct ProfRecord {
+  int kind;
+  int64_t items;
+  hipEvent_t start, end;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_pending;
+varlen_attn_profile_t g_prof_totals;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` between two recorded events when profiling is on.
+template <class F>
+hipError_t timed(int kind, int64_t items, hipStream_t s, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    on = g_prof_on;
+  }
+  if (!on || items <= 0) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    a = prof_event();
+    b = prof_event();
+  }
+  if (!a || !b) return launch();
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (e == hipSuccess) {
+    g_prof_pending.push_back({kind, items, a, b});
+  } else {
+    g_prof_pool.push_back(a);
+    g_prof_pool.push_back(b);
+  }
+  return e;
+}
+
 varlen_status_t hip_fail(hipError_t e, const char* what) {
   return fail(e == hipErrorOutOfMemory ? VARLEN_ERR_OUT_OF_MEMORY : VARLEN_ERR_DEVICE, "%s failed: %s", what,
               hipGetErrorString(e));
@@ -478,7 +532,9 @@ varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* 
 
   char* base = static_cast<char*>(ds.dev);
   WorkItem* dev_items = reinterpret_cast<WorkItem*>(base + lay.items_off);
-  PVA_HIP(hipMemcpyAsync(dev_items, stage, item_bytes, hipMemcpyHostToDevice, stream), "uploading the work list");
+  PVA_HIP(timed(4, (int64_t)item_bytes, stream,
+                [&] { return hipMemcpyAsync(dev_items, stage, item_bytes, hipMemcpyHostToDevice, stream); }),
+          "uploading the work list");
   PVA_HIP(hipEventRecord(ds.copied, stream), "hipEventRecord");
   ds.pending = true;
 
@@ -506,14 +562,17 @@ varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* 
     p.tanh_log2 = 2.f * pr.scale / pr.softcap * log2e;
   }
 
-  hipError_t e = hipSuccess;
+  const int n_pre = (int)plan.prefill.size(), n_dec = (int)plan.decode.size();
+  const int n_f32 = (int)plan.f32.size(), n_cmb = (int)plan.combine.size();
+  hipError_t e = timed(0, n_pre, stream, [&] {
+    return pva::launch_prefill_mfma(p, dev_items + off_prefill, n_pre, pr.dtype, plan.prefill_waves, stream);
+  });
   if (e == hipSuccess)
-    e = pva::launch_prefill_mfma(p, dev_items + off_prefill, (int)plan.prefill.size(), pr.dtype,
-                                 plan.prefill_waves, stream);
-  if (e == hipSuccess) e = pva::launch_decode(p, dev_items + off_decode, (int)plan.decode.size(), pr.dtype, stream);
-  if (e == hipSuccess) e = pva::launch_prefill_f32(p, dev_items + off_f32, (int)plan.f32.size(), stream);
+    e = timed(2, n_dec, stream, [&] { return pva::launch_decode(p, dev_items + off_decode, n_dec, pr.dtype, stream); });
   if (e == hipSuccess)
-    e = pva::launch_combine(p, dev_items + off_combine, (int)plan.combine.size(), pr.dtype, stream);
+    e = timed(1, n_f32, stream, [&] { return pva::launch_prefill_f32(p, dev_items + off_f32, n_f32, stream); });
+  if (e == hipSuccess)
+    e = timed(3, n_cmb, stream, [&] { return pva::launch_combine(p, dev_items + off_combine, n_cmb, pr.dtype, stream); });
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   PVA_HIP(hipEventRecord(ds.done, stream), "hipEventRecord");
   return VARLEN_OK;
@@ -636,5 +695,40 @@ varlen_status_t varlen_attn_release(void) {
 }
 
 const char* varlen_attn_version(void) { return "0.1.0"; }
+
+varlen_status_t varlen_attn_profile_enable(int32_t enable) {
+  g_last_error.clear();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (enable) {
+    for (auto& r : g_prof_pending) {
+      (void)hipEventSynchronize(r.end);
+      g_prof_pool.push_back(r.start);
+      g_prof_pool.push_back(r.end);
+    }
+    g_prof_pending.clear();
+    std::memset(&g_prof_totals, 0, sizeof g_prof_totals);
+  }
+  g_prof_on = enable != 0;
+  return VARLEN_OK;
+}
+
+varlen_status_t varlen_attn_profile_read(varlen_attn_profile_t* out) {
+  g_last_error.clear();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_pending) {
+    hipError_t e = hipEventSynchronize(r.end);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.end);
+    if (e != hipSuccess) return hip_fail(e, "reading kernel timing events");
+    g_prof_totals.total_ms[r.kind] += ms;
+    g_prof_totals.launches[r.kind] += 1;
+    g_prof_totals.items[r.kind] += r.items;
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.end);
+  }
+  g_prof_pending.clear();
+  if (out) *out = g_prof_totals;
+  return VARLEN_OK;
+}
 
 }  // extern "C"

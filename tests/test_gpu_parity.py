@@ -214,3 +214,23 @@ def test_full_size_workloads_sampled(name):
     assert torch.isfinite(out.float()).all()
     del batch, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_scores_rising_after_first_tile(dtype):
+    """Keys after the first 64 score far higher (by ~40 in natural-log units)
+    than the first tile's: the prefill kernel must redo such items with the
+    running-max softmax, and the result must still match the oracle."""
+    import torch
+    w = _workload(dtype=dtype, hq=8, hkv=2, causal=False)
+    lq, lkv = [40, 70], [300, 200]
+    batch = _batch(w, lq, lkv)
+    tdt = batch.q.dtype
+    batch.q[:] = 0.5
+    batch.k[:] = 0.01
+    k1 = int(batch.cu_kv[1])
+    batch.k[64:k1] = (torch.arange(64, k1, device="cuda").float() / k1 * 2.0).view(-1, 1, 1).to(tdt)
+    batch.k[k1 + 64:] = 1.5
+    _say("rising scores", dtype)
+    got = run_gpu(batch).double().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv)
+    compare(got, oracle_all(batch), w.dtype)
