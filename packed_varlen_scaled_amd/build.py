@@ -64,8 +64,21 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    missing = undefined_kernel_stubs(tmp)
+    if missing:
+        os.unlink(tmp)
+        raise RuntimeError("kernel launch stubs left undefined (a kernel body was dropped by the host "
+                           "compile): " + ", ".join(missing[:4]))
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def undefined_kernel_stubs(lib_path: str):
+    """Names of kernel launch stubs the library references but does not define."""
+    nm = shutil.which("nm") or os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "llvm-nm")
+    res = subprocess.run([nm, "-C", lib_path], capture_output=True, text=True, check=True)
+    return [line.split(" U ", 1)[1] for line in res.stdout.splitlines()
+            if " U " in line and "__device_stub__" in line]
 
 
 def main(argv=None) -> int:

@@ -161,6 +161,12 @@ __device__ __forceinline__ float sum2(uint32_t w, float acc) {
   }
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at ldst + 16*i, ldst being uniform across the wave.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
+  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
+}
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each group of 16
 // lanes, lane i receives element i % 4 of the 4-element rows addressed by
 // lanes 4j + i/4, j = 0..3: when lanes 4j..4j+3 address consecutive

@@ -24,11 +24,12 @@
 //     (v_permlane32_swap);
 //   * softmax in registers in log2 units (exp2 with log2(e) folded into the
 //     scale). Each row's first tile fixes a reference max and every later P
-//     is taken against it, so O is never rescaled inside the loop (P stays
-//     below 2^TAU, which bf16 / f16 and the fp32 accumulators hold); a
-//     workgroup whose scores climb past that bound redoes its item with the
-//     textbook running-max softmax. Either way the result is the same
-//     softmax up to rounding;
+//     is taken against it, so O is never rescaled and no tile max is taken
+//     inside the loop: bf16 P and the fp32 accumulators have fp32's exponent
+//     range. A workgroup whose l or O overflowed (scores rising ~2^127 above
+//     the first tile's, or ~2^16 for f16 P) redoes its item with the textbook
+//     running-max softmax. Either way the result is the same softmax up to
+//     rounding;
 //   * O^T += V^T . P^T on 32x32x16 MFMA, P rounded to the I/O type with the
 //     score accumulator registers reused directly as the B operand (the
 //     MFMA reduction order over keys is free, so V^T is read in the order
@@ -72,9 +73,6 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   constexpr int BLOCKS = BN / ROWS_PER_BLOCK;
   constexpr int BPW = BLOCKS / NW;         // 1 KB blocks per wave per tile (K and V each)
   static_assert(BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
-  // Largest exponent P may take above 1 without a rescale: bf16 shares fp32's
-  // exponent range; f16 tops out near 2^16.
-  constexpr float TAU = BF16 ? 20.0f : 15.0f;
 
   // K0 K1 V0 V1, each [key][d] with 16-byte chunk c of row r stored at chunk
   // c ^ chunk_perm<D>(r).
@@ -83,7 +81,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int hh = wave % it.heads;
@@ -118,7 +116,6 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
   float m_ref = ninf();  // reference max of the row (log2 units)
   float l_run = 0.f;     // this lane's half of the row sum
-  bool overflow = false;
 
   // ---- HBM -> LDS tile loads ------------------------------------------------
   // Wave w fills 1 KB blocks w, w + NW, ... of each tile; lane L of a block
@@ -134,6 +131,15 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const uint32_t dma_off = (uint32_t)((blk_row * tok_stride + dma_chunk * 8) * 2);
   const uint32_t dma_step = (uint32_t)(NW * ROWS_PER_BLOCK * tok_stride * 2);  // bytes between this wave's blocks
 
+  // One 1 KB block (index i of this wave's BPW) of the K or V tile at kt.
+  auto issue_k_block = [&](int kt, int buf, int i) {
+    const char* kb = kbase + (int64_t)kt * tok_stride * 2;
+    lds_dma16(kb + dma_off + i * dma_step, lds + buf * TILE + wave * 512 + i * NW * 512);
+  };
+  auto issue_v_block = [&](int kt, int buf, int i) {
+    const char* vb = vbase + (int64_t)kt * tok_stride * 2;
+    lds_dma16(vb + dma_off + i * dma_step, lds + (2 + buf) * TILE + wave * 512 + i * NW * 512);
+  };
   auto issue_tile = [&](int kt, int buf) {
     const char* kb = kbase + (int64_t)kt * tok_stride * 2;
     const char* vb = vbase + (int64_t)kt * tok_stride * 2;
@@ -143,8 +149,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     if (rows >= BN) {
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
-        __builtin_amdgcn_global_load_lds(kb + dma_off + i * dma_step, kl + i * NW * 512, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + dma_off + i * dma_step, vl + i * NW * 512, 16, 0, 0);
+        lds_dma16(kb + dma_off + i * dma_step, kl + i * NW * 512);
+        lds_dma16(vb + dma_off + i * dma_step, vl + i * NW * 512);
       }
     } else {
       // last tile: rows at or past kv_end are zeros (never the next sequence)
@@ -152,8 +158,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       for (int i = 0; i < BPW; ++i) {
         const int r = blk_row + i * NW * ROWS_PER_BLOCK;
         if (r < rows) {
-          __builtin_amdgcn_global_load_lds(kb + dma_off + i * dma_step, kl + i * NW * 512, 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vb + dma_off + i * dma_step, vl + i * NW * 512, 16, 0, 0);
+          lds_dma16(kb + dma_off + i * dma_step, kl + i * NW * 512);
+          lds_dma16(vb + dma_off + i * dma_step, vl + i * NW * 512);
         } else {
           const u32x4_t zero = {0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4_t*>(kl + i * NW * 512 + 8 * lane) = zero;
@@ -187,11 +193,14 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   //   kPlain  - a tile that needs no mask for any row of the workgroup;
   //   kMasked - a tile that crosses the causal frontier or kv_end;
   //   kSafe   - the textbook online softmax (masked, running max, O rescaled
-  //             on every tile), used only to redo an item whose scores rose
-  //             more than 2^TAU above the first tile's.
-  // Outside kSafe, P = 2^(y - m_ref) stays below 2^TAU: bf16 and fp32 have
-  // the range for that, and O is never rescaled inside the loop.
-  auto compute = [&](int buf, int kt, auto mode_tag) {
+  //             on every tile), used only to redo an item whose P, l or O
+  //             overflowed against the first tile's max.
+  // Outside kSafe, P = 2^(y - m_ref) with no running max: O is never
+  // rescaled and no max is taken inside the loop.
+  // dma_kt >= 0: while computing, stream the (full) tile at dma_kt into the
+  // other buffer, one 1 KB block at a time between MFMA groups, so that the
+  // load path drains behind the math instead of stalling the wave.
+  auto compute = [&](int buf, int kt, auto mode_tag, int dma_kt) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr bool MASK = MODE != kPlain;
     const uint16_t* ks = lds + buf * TILE;
@@ -215,6 +224,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     for (int kk = 0; kk < KPF - 1 && kk < KSTEPS; ++kk) load_k(kk);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kk % (KSTEPS / BPW) == 0 && dma_kt >= 0) issue_k_block(dma_kt, buf ^ 1, kk / (KSTEPS / BPW));
       if (kk + KPF - 1 < KSTEPS) load_k(kk + KPF - 1);
 #pragma unroll
       for (int mt = 0; mt < BN / 32; ++mt) sacc[mt] = mfma32<BF16>(kfr[kk % KPF][mt], qf[kk], sacc[mt]);
@@ -234,31 +244,31 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
         }
       }
     }
-    float mx = ninf();
+    if constexpr (MODE == kFirst || MODE == kSafe) {
+      float mx = ninf();
 #pragma unroll
-    for (int mt = 0; mt < BN / 32; ++mt) {
+      for (int mt = 0; mt < BN / 32; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sacc[mt][r]), sacc[mt][r + 1]);
-    }
-    mx = max_with_partner32(mx);
-    float tmax;
-    if constexpr (SOFTCAP) {
-      tmax = (mx == ninf()) ? ninf()
-                            : p.cap_log2 * (1.f - 2.f * rcp_fast(exp2_fast(mx * p.tanh_log2) + 1.f));
-    } else {
-      tmax = mx * p.score_log2;
-    }
-    if constexpr (MODE == kFirst) {
-      m_ref = tmax;
-    } else if constexpr (MODE == kSafe) {
-      const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = (m_new == ninf()) ? 1.f : exp2_fast(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sacc[mt][r]), sacc[mt][r + 1]);
+      }
+      mx = max_with_partner32(mx);
+      float tmax;
+      if constexpr (SOFTCAP) {
+        tmax = (mx == ninf()) ? ninf()
+                              : p.cap_log2 * (1.f - 2.f * rcp_fast(exp2_fast(mx * p.tanh_log2) + 1.f));
+      } else {
+        tmax = mx * p.score_log2;
+      }
+      if constexpr (MODE == kFirst) {
+        m_ref = tmax;
+      } else {
+        const float m_new = fmaxf(m_ref, tmax);
+        const float alpha = (m_new == ninf()) ? 1.f : exp2_fast(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
-    } else {
-      overflow = overflow || (tmax > m_ref + TAU);
+        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+      }
     }
     const float m_use = (m_ref == ninf()) ? 0.f : m_ref;
 
@@ -302,6 +312,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
     for (int kb = 0; kb < BN / 16; ++kb) {
+      if (kb % ((BN / 16) / BPW) == 0 && dma_kt >= 0) issue_v_block(dma_kt, buf ^ 1, kb / ((BN / 16) / BPW));
       u32x4_t a[D / 32];
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
@@ -333,10 +344,19 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   }
   auto step = [&](int t) {
     const int kt = kv_begin + t * BN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(kt + BN, (t + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t have landed
+    __syncthreads();                      // ... and every wave's; the other buffer is free again
     return kt;
+  };
+  // Start of the next tile: a full one is streamed during the compute (or
+  // right away by a wave that skips the compute); a partial last tile, which
+  // needs its zero rows written, is issued at once.
+  auto next_full = [&](int t) -> int {
+    if (t + 1 >= n_tiles) return -1;
+    const int kn = kv_begin + (t + 1) * BN;
+    if (kn + BN <= kv_end) return kn;
+    issue_tile(kn, (t + 1) & 1);
+    return -1;
   };
   auto run_pass = [&](auto safe_tag) {
     constexpr bool SAFE = decltype(safe_tag)::value;
@@ -344,35 +364,55 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     if constexpr (SAFE) {
       for (int t = 0; t < n_tiles; ++t) {
         const int kt = step(t);
-        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kSafe>{});
+        const int dk = next_full(t);
+        if (wave_active && !(p.causal && kt > wave_last + off)) {
+          compute(t & 1, kt, std::integral_constant<int, kSafe>{}, dk);
+        } else if (dk >= 0) {
+          issue_tile(dk, (t + 1) & 1);
+        }
       }
     } else {
       if (n_tiles > 0) {
         const int kt = step(0);
-        compute(0, kt, std::integral_constant<int, kFirst>{});
+        compute(0, kt, std::integral_constant<int, kFirst>{}, next_full(0));
       }
       for (int t = 1; t < n_plain; ++t) {
         const int kt = step(t);
-        compute(t & 1, kt, std::integral_constant<int, kPlain>{});
+        compute(t & 1, kt, std::integral_constant<int, kPlain>{}, next_full(t));
       }
       for (int t = max(n_plain, 1); t < n_tiles; ++t) {
         const int kt = step(t);
-        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
+        const int dk = next_full(t);
+        if (wave_active && !(p.causal && kt > wave_last + off)) {
+          compute(t & 1, kt, std::integral_constant<int, kMasked>{}, dk);
+        } else if (dk >= 0) {
+          issue_tile(dk, (t + 1) & 1);
+        }
       }
     }
   };
 
   run_pass(std::false_type{});
-  // Redo the item with the rescaling softmax if any row's scores rose more
-  // than 2^TAU above its first tile's (decided for the whole workgroup: the
-  // tiles are loaded by all of its waves).
-  __syncthreads();
-  if (__syncthreads_or(__any(overflow && row_ok) ? 1 : 0)) {
+  // P was taken against each row's first-tile max without any bound. If a
+  // later score rose so far above it that P, l or O overflowed, the item is
+  // redone with the rescaling softmax (decided for the whole workgroup: the
+  // tiles are loaded by all of its waves). chk is NaN/inf iff l or an O
+  // element is.
+  {
+    float chk = sum_with_partner32(l_run);
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
-    m_ref = ninf();
-    l_run = 0.f;
-    run_pass(std::true_type{});
+    for (int mb = 0; mb < D / 32; ++mb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) chk = __builtin_fmaf(oacc[mb][r], 0.f, chk);
+    }
+    const bool bad = wave_active && row_ok && !__builtin_isfinite(chk);
+    if (__syncthreads_or(__any(bad) ? 1 : 0)) {
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
+      m_ref = ninf();
+      l_run = 0.f;
+      run_pass(std::true_type{});
+    }
   }
 
   if (!wave_active || !row_ok) return;

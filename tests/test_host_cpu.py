@@ -39,6 +39,13 @@ def test_library_exports_every_declared_symbol():
     assert pva.version().count(".") == 2
 
 
+def test_library_defines_every_kernel_launch_stub():
+    """A kernel whose host stub is missing would link (undefined symbols are
+    allowed in a shared library) and fail only when launched."""
+    from packed_varlen_scaled_amd import build as b
+    assert b.undefined_kernel_stubs(pva.library_path()) == []
+
+
 def _cu(lengths):
     return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
 
