@@ -167,6 +167,31 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
   __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
 }
 
+// The same load issued as inline assembly (M0 = lds_base, which must be
+// wave-uniform; lane i's bytes land at lds_base + 16*i). The compiler then
+// does not count it among the wave's outstanding vector-memory loads, so it
+// adds no vmcnt wait of its own before later LDS reads (it cannot tell which
+// LDS bytes such a load writes and would otherwise wait after every one).
+// Whoever issues it orders it explicitly: an s_waitcnt vmcnt covering the
+// load, then a workgroup barrier, before any wave reads the bytes. The
+// compiler's own vmcnt waits stay correct (loads retire in order, so an
+// extra load issued in between only makes them wait longer).
+__device__ __forceinline__ void lds_dma16_async(const void* gsrc, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds_base)
+      : "memory", "m0");
+}
+// LDS byte address of a pointer into a __shared__ array (wave-uniform when
+// the pointer is).
+__device__ __forceinline__ uint32_t lds_addr32(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p));
+}
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16). Within each group of 16
 // lanes, lane i receives element i % 4 of the 4-element rows addressed by
 // lanes 4j + i/4, j = 0..3: when lanes 4j..4j+3 address consecutive

@@ -131,15 +131,6 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const uint32_t dma_off = (uint32_t)((blk_row * tok_stride + dma_chunk * 8) * 2);
   const uint32_t dma_step = (uint32_t)(NW * ROWS_PER_BLOCK * tok_stride * 2);  // bytes between this wave's blocks
 
-  // One 1 KB block (index i of this wave's BPW) of the K or V tile at kt.
-  auto issue_k_block = [&](int kt, int buf, int i) {
-    const char* kb = kbase + (int64_t)kt * tok_stride * 2;
-    lds_dma16(kb + dma_off + i * dma_step, lds + buf * TILE + wave * 512 + i * NW * 512);
-  };
-  auto issue_v_block = [&](int kt, int buf, int i) {
-    const char* vb = vbase + (int64_t)kt * tok_stride * 2;
-    lds_dma16(vb + dma_off + i * dma_step, lds + (2 + buf) * TILE + wave * 512 + i * NW * 512);
-  };
   auto issue_tile = [&](int kt, int buf) {
     const char* kb = kbase + (int64_t)kt * tok_stride * 2;
     const char* vb = vbase + (int64_t)kt * tok_stride * 2;
@@ -149,8 +140,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     if (rows >= BN) {
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
-        lds_dma16(kb + dma_off + i * dma_step, kl + i * NW * 512);
-        lds_dma16(vb + dma_off + i * dma_step, vl + i * NW * 512);
+        lds_dma16_async(kb + dma_off + i * dma_step, lds_addr32(kl + i * NW * 512));
+        lds_dma16_async(vb + dma_off + i * dma_step, lds_addr32(vl + i * NW * 512));
       }
     } else {
       // last tile: rows at or past kv_end are zeros (never the next sequence)
@@ -158,8 +149,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       for (int i = 0; i < BPW; ++i) {
         const int r = blk_row + i * NW * ROWS_PER_BLOCK;
         if (r < rows) {
-          lds_dma16(kb + dma_off + i * dma_step, kl + i * NW * 512);
-          lds_dma16(vb + dma_off + i * dma_step, vl + i * NW * 512);
+          lds_dma16_async(kb + dma_off + i * dma_step, lds_addr32(kl + i * NW * 512));
+          lds_dma16_async(vb + dma_off + i * dma_step, lds_addr32(vl + i * NW * 512));
         } else {
           const u32x4_t zero = {0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4_t*>(kl + i * NW * 512 + 8 * lane) = zero;
@@ -197,10 +188,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   //             overflowed against the first tile's max.
   // Outside kSafe, P = 2^(y - m_ref) with no running max: O is never
   // rescaled and no max is taken inside the loop.
-  // dma_kt >= 0: while computing, stream the (full) tile at dma_kt into the
-  // other buffer, one 1 KB block at a time between MFMA groups, so that the
-  // load path drains behind the math instead of stalling the wave.
-  auto compute = [&](int buf, int kt, auto mode_tag, int dma_kt) {
+  auto compute = [&](int buf, int kt, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr bool MASK = MODE != kPlain;
     const uint16_t* ks = lds + buf * TILE;
@@ -224,7 +212,6 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     for (int kk = 0; kk < KPF - 1 && kk < KSTEPS; ++kk) load_k(kk);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (kk % (KSTEPS / BPW) == 0 && dma_kt >= 0) issue_k_block(dma_kt, buf ^ 1, kk / (KSTEPS / BPW));
       if (kk + KPF - 1 < KSTEPS) load_k(kk + KPF - 1);
 #pragma unroll
       for (int mt = 0; mt < BN / 32; ++mt) sacc[mt] = mfma32<BF16>(kfr[kk % KPF][mt], qf[kk], sacc[mt]);
@@ -312,7 +299,6 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
     for (int kb = 0; kb < BN / 16; ++kb) {
-      if (kb % ((BN / 16) / BPW) == 0 && dma_kt >= 0) issue_v_block(dma_kt, buf ^ 1, kb / ((BN / 16) / BPW));
       u32x4_t a[D / 32];
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
@@ -328,7 +314,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   // ---- key-tile loops ----------------------------------------------------------
   // Every loop step: wait for this wave's loads of the current tile, one
   // barrier (all waves' loads landed; the other buffer is free again), start
-  // streaming the next tile into the other buffer, compute the current one.
+  // loading the next tile into the other buffer, compute the current one.
   const int n_tiles = (kv_end - kv_begin + BN - 1) / BN;
   // Tiles [1, n_plain) need no mask for any row of the workgroup: they end at
   // or before kv_end and before the first row's causal frontier.
@@ -346,17 +332,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     const int kt = kv_begin + t * BN;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t have landed
     __syncthreads();                      // ... and every wave's; the other buffer is free again
+    if (t + 1 < n_tiles) issue_tile(kt + BN, (t + 1) & 1);
     return kt;
-  };
-  // Start of the next tile: a full one is streamed during the compute (or
-  // right away by a wave that skips the compute); a partial last tile, which
-  // needs its zero rows written, is issued at once.
-  auto next_full = [&](int t) -> int {
-    if (t + 1 >= n_tiles) return -1;
-    const int kn = kv_begin + (t + 1) * BN;
-    if (kn + BN <= kv_end) return kn;
-    issue_tile(kn, (t + 1) & 1);
-    return -1;
   };
   auto run_pass = [&](auto safe_tag) {
     constexpr bool SAFE = decltype(safe_tag)::value;
@@ -364,30 +341,14 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     if constexpr (SAFE) {
       for (int t = 0; t < n_tiles; ++t) {
         const int kt = step(t);
-        const int dk = next_full(t);
-        if (wave_active && !(p.causal && kt > wave_last + off)) {
-          compute(t & 1, kt, std::integral_constant<int, kSafe>{}, dk);
-        } else if (dk >= 0) {
-          issue_tile(dk, (t + 1) & 1);
-        }
+        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kSafe>{});
       }
     } else {
-      if (n_tiles > 0) {
-        const int kt = step(0);
-        compute(0, kt, std::integral_constant<int, kFirst>{}, next_full(0));
-      }
-      for (int t = 1; t < n_plain; ++t) {
-        const int kt = step(t);
-        compute(t & 1, kt, std::integral_constant<int, kPlain>{}, next_full(t));
-      }
+      if (n_tiles > 0) compute(0, step(0), std::integral_constant<int, kFirst>{});
+      for (int t = 1; t < n_plain; ++t) compute(t & 1, step(t), std::integral_constant<int, kPlain>{});
       for (int t = max(n_plain, 1); t < n_tiles; ++t) {
         const int kt = step(t);
-        const int dk = next_full(t);
-        if (wave_active && !(p.causal && kt > wave_last + off)) {
-          compute(t & 1, kt, std::integral_constant<int, kMasked>{}, dk);
-        } else if (dk >= 0) {
-          issue_tile(dk, (t + 1) & 1);
-        }
+        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
       }
     }
   };
