@@ -152,6 +152,44 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0):
                       f"{reps} pass(es), {dt * reps:.1f} s"}
 
 
+def gemm_ceiling() -> int:
+    """bf16 GEMM throughput by operand data. MFMA throughput on this chip
+    depends on the operand bits (the clock drops as more bits toggle), so the
+    dense spec peak is reached only on near-constant data."""
+    import torch
+    n = 8192
+    torch.manual_seed(0)
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    res = {}
+    for kind in ("zeros", "ones", "normal"):
+        if kind == "zeros":
+            a = torch.zeros(n, n, dtype=torch.bfloat16, device="cuda:0")
+            b = torch.zeros(n, n, dtype=torch.bfloat16, device="cuda:0")
+        elif kind == "ones":
+            a = torch.ones(n, n, dtype=torch.bfloat16, device="cuda:0")
+            b = torch.ones(n, n, dtype=torch.bfloat16, device="cuda:0")
+        else:
+            a = torch.randn(n, n, dtype=torch.float32, device="cuda:0", generator=g).to(torch.bfloat16)
+            b = torch.randn(n, n, dtype=torch.float32, device="cuda:0", generator=g).to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        reps = 30
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * n ** 3 / (ms / 1e3) / 1e12
+        res[kind] = {"ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+        log(f"[gemm] {kind}: {ms:.3f} ms {tf:.0f} TFLOP/s")
+        del a, b
+    print(json.dumps({"gemm_ceiling": res, "m=n=k": n, "dtype": "bf16", "peak": PEAK_BF16_TFLOPS}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,7 +201,13 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes, 5 times (the known-size "
                          "reference that HBM byte counters are calibrated against), then exit")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time a plain library bf16 GEMM (8192^3, torch.matmul -> hipBLASLt) on "
+                         "zero, constant and N(0,1) operands, then exit: the MFMA rate the chip sustains "
+                         "on data like the workloads', next to the dense spec peak")
     a = ap.parse_args(argv)
+    if a.gemm_ceiling:
+        return gemm_ceiling()
     if a.copy_reference:
         import torch
         n = a.copy_reference << 20

@@ -234,3 +234,36 @@ def test_scores_rising_after_first_tile(dtype):
     _say("rising scores", dtype)
     got = run_gpu(batch).double().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv)
     compare(got, oracle_all(batch), w.dtype)
+
+
+def test_back_to_back_calls_on_two_streams():
+    """Calls issued without synchronising, alternating two streams and three
+    problem sizes (with split-KV partials): the work-list slots and the
+    partials buffer are reused while earlier calls may still run, and every
+    result must equal the same call made alone."""
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = _workload(hq=16, hkv=2, softcap=20.0)
+    shapes = [([1, 100, 1, 257, 1], [1000, 700, 129, 300, 5]), ([64, 1, 300], [64, 4000, 300]),
+              ([1] * 9, [300 + 500 * i for i in range(9)])]
+    batches = [_batch(w, lq, lkv) for lq, lkv in shapes]
+    alone = [run_gpu(b).clone() for b in batches]
+
+    def call(b, out):
+        cu_q = torch.from_numpy(b.cu_q).cuda()
+        cu_kv = torch.from_numpy(b.cu_kv).cuda()
+        pva.varlen_attn_fwd(b.q, b.k, b.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads, is_causal=True,
+                            softcap=w.softcap, out=out, cu_seqlens_q_host=b.cu_q, cu_seqlens_kv_host=b.cu_kv)
+
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(a) for a in alone] for _ in range(4)]
+    torch.cuda.synchronize()
+    _say("two streams, 12 calls")
+    for r in range(4):
+        for i, b in enumerate(batches):
+            with torch.cuda.stream(streams[(r * 3 + i) % 2]):
+                call(b, outs[r][i])
+    torch.cuda.synchronize()
+    for r in range(4):
+        for i in range(3):
+            assert torch.equal(outs[r][i], alone[i]), (r, i)
