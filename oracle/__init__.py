@@ -19,6 +19,10 @@ page src/kernels/standard_attention.rs, "Semantics"):
   ``1/sqrt(head_size)``;
 * ``s = softcap*tanh(s/softcap)`` when softcap is non-zero, before the mask;
 * with ``is_causal``, key j is visible to query i iff ``j <= i + L_kv - L_q``;
+* with a local window ``W > 0`` (causal or not), key j is visible only if
+  ``j >= i + L_kv - L_q + 1 - W`` (page src/kernels/attention.rs, the softmax
+  kernel source's local_min; page src/kernels/group_query_attention.rs, the
+  local_window_size attribute);
 * stable softmax over the visible keys, rows with no visible key are zero;
 * ``out = softmax . V`` in fp64.
 """
@@ -62,7 +66,7 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_int, ctypes.c_double,
-            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.pva_oracle_default_threads.restype = ctypes.c_int
@@ -114,7 +118,7 @@ def _as_host_array(x, dtype: str) -> np.ndarray:
 def attention(q, k, v, cu_q, cu_kv, num_heads: int, kv_num_heads: int | None = None,
               scale: float | None = None, is_causal: bool = False, softcap: float = 0.0,
               dtype: str = "f32", rows=None, key_window=None, with_lse: bool = False,
-              threads: int = 0):
+              threads: int = 0, local_window: int = 0):
     """Run the fp64 oracle.
 
     q: [total_q, Hq*D] or [total_q, Hq, D]; k: [total_kv, Hkv, D]; v: [total_kv, Hkv, Dv]
@@ -122,6 +126,7 @@ def attention(q, k, v, cu_q, cu_kv, num_heads: int, kv_num_heads: int | None = N
     cu_q, cu_kv: int sequences of length B+1.
     scale: None or 0 -> 1/sqrt(D). rows: optional int64 row ids (token*Hq + head).
     key_window: optional (begin, end) local key window applied to every sequence.
+    local_window: W > 0 limits row i to keys j >= i + L_kv - L_q + 1 - W; <= 0 no window.
     Returns out [n_rows, Dv] fp64 (and lse [n_rows] when ``with_lse``).
     """
     lib = _load()
@@ -168,7 +173,7 @@ def attention(q, k, v, cu_q, cu_kv, num_heads: int, kv_num_heads: int | None = N
     rc = lib.pva_oracle_attention(
         ptr(qa), ptr(ka), ptr(va), DTYPE_CODES[dtype],
         cuq.ctypes.data, cukv.ctypes.data, batch, total_q, total_kv, hq, hkv, d, dv,
-        _f32(scale) if scale else 0.0, 1 if is_causal else 0, _f32(softcap),
+        _f32(scale) if scale else 0.0, 1 if is_causal else 0, _f32(softcap), int(local_window),
         rows_ptr, n_rows, kb, ke,
         ptr(out), (ptr(lse) if lse is not None else None), int(threads))
     if rc != 0:

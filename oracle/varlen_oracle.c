@@ -9,7 +9,9 @@
  *
  * Sources (the crate onnx-runtime-ep-cuda, docs.rs source pages):
  *   [PVA] src/kernels/packed_varlen_attention.rs (0.1.0-dev.6)
+ *   [ATT] src/kernels/attention.rs                (0.1.0-dev.6)
  *   [STD] src/kernels/standard_attention.rs       (latest page, 0.1.0-dev.5)
+ *   [GQA] src/kernels/group_query_attention.rs    (latest page)
  *
  * What is computed, for every sequence b of the packed batch, every query
  * head h and every query row i of that sequence (plain definition, written
@@ -30,6 +32,15 @@
  *   s_j = -inf  iff causal and j > i + (L_kv - L_q)
  *                                                 [PVA] "Causal alignment",
  *                                                 row kernel stage 3
+ *   s_j = -inf  iff W > 0 and j < i + (L_kv - L_q) + 1 - W
+ *                                                 (local window of W keys
+ *                                                 ending at the row's
+ *                                                 tail-aligned diagonal, with
+ *                                                 or without the causal mask:
+ *                                                 [ATT] softmax kernel source,
+ *                                                 local_min; [GQA] the
+ *                                                 local_window_size attribute
+ *                                                 and the kernel's local_start)
  *   m = max_j s_j; a row with no keys or m = -inf is all zeros;
  *   otherwise e_j = exp(s_j - m), l = sum_j e_j,
  *   O[q0+i,h,c] = sum_j e_j * V[k0+j,g,c] / l     [PVA] row kernel stages 4-5;
@@ -91,6 +102,7 @@ typedef struct {
   int32_t batch, hq, hkv, d, dv;
   double scale, softcap;
   int causal;
+  int32_t local_window; /* <= 0: no window */
   int32_t key_begin, key_end;
   const int64_t* rows; /* row id = token * hq + head; NULL -> all rows */
   int64_t n_rows;
@@ -150,6 +162,9 @@ static void attend_row(const oracle_job* job, int64_t t, int32_t h, double* s,
     if (job->causal && j > i + offset) {
       acc = -INFINITY;
     }
+    if (job->local_window > 0 && j < i + offset + 1 - job->local_window) {
+      acc = -INFINITY;
+    }
     s[j - j0] = acc;
     if (acc > m) m = acc;
   }
@@ -200,6 +215,8 @@ static void* worker_main(void* arg) {
  *      storage type dtype (0 f32, 1 f16, 2 bf16), contiguous, host memory.
  *   cu_q, cu_kv: int32 [batch + 1] exclusive prefix sums.
  *   scale: the caller's scale; 0 selects 1/sqrt(d).
+ *   local_window: W > 0 restricts row i to keys j >= i + L_kv - L_q + 1 - W;
+ *         <= 0 means no window.
  *   rows: NULL for all total_q*hq rows in (token, head) order, else n_rows
  *         row ids (token * hq + head).
  *   key_begin/key_end: local key window per sequence (-1, -1 for all keys).
@@ -211,7 +228,7 @@ int pva_oracle_attention(const void* q, const void* k, const void* v, int dtype,
                          const int32_t* cu_q, const int32_t* cu_kv, int32_t batch,
                          int64_t total_q, int64_t total_kv, int32_t hq, int32_t hkv,
                          int32_t d, int32_t dv, double scale, int causal, double softcap,
-                         const int64_t* rows, int64_t n_rows, int32_t key_begin,
+                         int32_t local_window, const int64_t* rows, int64_t n_rows, int32_t key_begin,
                          int32_t key_end, double* out, double* lse, int n_threads) {
   if (batch < 1 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || dv <= 0) return -1;
   if (dtype < ORACLE_F32 || dtype > ORACLE_BF16) return -1;
@@ -233,6 +250,7 @@ int pva_oracle_attention(const void* q, const void* k, const void* v, int dtype,
   job.hq = hq; job.hkv = hkv; job.d = d; job.dv = dv;
   job.scale = scale != 0.0 ? scale : 1.0 / sqrt((double)d);
   job.softcap = softcap; job.causal = causal != 0;
+  job.local_window = local_window;
   job.key_begin = key_begin; job.key_end = key_end;
   job.rows = rows; job.n_rows = n_rows; job.out = out; job.lse = lse;
   job.max_kv = max_kv;

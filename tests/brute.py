@@ -14,8 +14,11 @@ from __future__ import annotations
 import math
 
 
-def padded_attention(q, k, v, lq, lkv, hq, hkv, scale, causal, softcap):
+def padded_attention(q, k, v, lq, lkv, hq, hkv, scale, causal, softcap, window=0):
     """q: packed nested lists [total_q][hq][d]; k, v: [total_kv][hkv][*].
+
+    window > 0 keeps, for query i, only keys j with i - j < window - (lkv - lq)
+    (the last `window` keys up to its tail-aligned diagonal).
 
     Returns packed output [total_q][hq][dv] as Python floats."""
     bsz = len(lq)
@@ -40,7 +43,8 @@ def padded_attention(q, k, v, lq, lkv, hq, hkv, scale, causal, softcap):
     for b in range(bsz):
         # mask[i][j]: query i may see key j.
         mask = [[(i < lq[b] and j < lkv[b] and
-                  (not causal or j - i <= lkv[b] - lq[b]))
+                  (not causal or j - i <= lkv[b] - lq[b]) and
+                  (window <= 0 or i - j < window - (lkv[b] - lq[b])))
                  for j in range(skv)] for i in range(sq)]
         seq_out = [[None] * hq for _ in range(lq[b])]
         for h in range(hq):

@@ -2,7 +2,8 @@
 
 Each case copies the oracle's C source, plants one mistake (a wrong head
 mapping, a flipped causal offset, a dropped softcap, scale or normalisation,
-a transposed operand, an off-by-one mask, a wrong bf16 widening), builds the
+a transposed operand, an off-by-one mask, a wrong bf16 widening, a local window
+that is dropped, off by one or blind to the causal offset), builds the
 copy with gcc into a temporary directory and checks that the brute-force pin
 no longer agrees. The planted mistakes live only in the temporary copy.
 """
@@ -30,6 +31,9 @@ MUTATIONS = {
     "no_normalisation": ("out_row[c] /= l;", "out_row[c] /= 1.0;"),
     "bf16_widening": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     "wrong_sequence_owner": ("if (job->cu_q[mid] <= t) lo = mid;", "if (job->cu_q[mid] < t) lo = mid;"),
+    "window_off_by_one": ("j < i + offset + 1 - job->local_window", "j <= i + offset + 1 - job->local_window"),
+    "window_without_offset": ("j < i + offset + 1 - job->local_window", "j < i + 1 - job->local_window"),
+    "window_dropped": ("if (job->local_window > 0 && j <", "if (0 && j <"),
 }
 
 
@@ -48,17 +52,19 @@ def _build_mutant(tmp_path, name):
 def _pin_cases():
     rng = np.random.default_rng(99)
     cases = []
-    for causal, softcap, (hq, hkv), (lq, lkv) in [
-        (True, 0.0, (4, 2), ([3, 4], [5, 4])),
-        (True, 2.0, (4, 2), ([2, 3], [2, 6])),
-        (False, 1.5, (6, 3), ([3, 2], [4, 3])),
-        (True, 0.0, (2, 2), ([4], [2])),
+    for causal, softcap, (hq, hkv), (lq, lkv), window in [
+        (True, 0.0, (4, 2), ([3, 4], [5, 4]), 0),
+        (True, 2.0, (4, 2), ([2, 3], [2, 6]), 0),
+        (False, 1.5, (6, 3), ([3, 2], [4, 3]), 0),
+        (True, 0.0, (2, 2), ([4], [2]), 0),
+        (True, 0.0, (2, 1), ([3, 4], [6, 4]), 2),
+        (False, 1.0, (2, 2), ([4, 2], [5, 3]), 3),
     ]:
         d = 3
         q = (rng.standard_normal((sum(lq), hq, d)) * 2).astype(np.float32)
         k = (rng.standard_normal((sum(lkv), hkv, d)) * 2).astype(np.float32)
         v = rng.standard_normal((sum(lkv), hkv, d)).astype(np.float32)
-        cases.append((q, k, v, lq, lkv, hq, hkv, 0.5, causal, softcap))
+        cases.append((q, k, v, lq, lkv, hq, hkv, 0.5, causal, softcap, window))
     return cases
 
 
@@ -70,13 +76,13 @@ def _max_pin_error(lib_path):
         oracle._LIB_PATH = lib_path
         oracle.build = lambda force=False: lib_path  # noqa: E731 - do not rebuild the mutant
         worst = 0.0
-        for q, k, v, lq, lkv, hq, hkv, scale, causal, softcap in _pin_cases():
+        for q, k, v, lq, lkv, hq, hkv, scale, causal, softcap, window in _pin_cases():
             cu = lambda x: np.concatenate([[0], np.cumsum(x)]).astype(np.int32)  # noqa: E731
             got = oracle.attention(q, k, v, cu(lq), cu(lkv), hq, hkv, scale=scale,
-                                   is_causal=causal, softcap=softcap, dtype="f32")
+                                   is_causal=causal, softcap=softcap, dtype="f32", local_window=window)
             want = np.asarray(padded_attention(q.astype(float).tolist(), k.astype(float).tolist(),
                                                v.astype(float).tolist(), lq, lkv, hq, hkv, scale,
-                                               causal, softcap)).reshape(got.shape)
+                                               causal, softcap, window=window)).reshape(got.shape)
             worst = max(worst, float(np.max(np.abs(got - want))))
         return worst
     finally:

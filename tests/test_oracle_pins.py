@@ -362,3 +362,71 @@ def test_oracle_rejects_inconsistent_arguments():
         _run(q, k, v, [3], [3], 4, 3, 1.0, False, 0.0)  # 3 does not divide 4
     with pytest.raises(ValueError):
         oracle.attention(q, k, v, [0, 2], [0, 3], 4, 3, dtype="f32")  # cu_q[B] != total
+
+
+# --------------------------------------------------------------------------
+# Local window (page src/kernels/attention.rs, the softmax kernel source's
+# local_min; page src/kernels/group_query_attention.rs, local_window_size).
+# --------------------------------------------------------------------------
+WINDOW_CASES = []
+for causal, window, softcap, lens in itertools.product(
+        [False, True], [1, 2, 3, 5], [0.0, 2.5],
+        [([4], [4]), ([2, 5, 1], [2, 5, 1]), ([3, 1, 4], [6, 2, 7]), ([6, 2], [3, 0]), ([7, 3], [4, 7])]):
+    WINDOW_CASES.append((causal, window, softcap, lens))
+
+
+@pytest.mark.parametrize("causal,window,softcap,lens", WINDOW_CASES)
+def test_window_matches_padded_brute_force(causal, window, softcap, lens):
+    lq, lkv = lens
+    rng = np.random.default_rng(hash((causal, window, softcap, str(lens))) & 0xFFFF)
+    hq, hkv, d, dv = 4, 2, 3, 2
+    tq, tkv = sum(lq), sum(lkv)
+    q, k, v = _rand((tq, hq, d), rng), _rand((tkv, hkv, d), rng), _rand((tkv, hkv, dv), rng)
+    got = _run(q, k, v, lq, lkv, hq, hkv, 0.7, causal, softcap, local_window=window)
+    want = padded_attention(q.astype(np.float64).tolist(), k.astype(np.float64).tolist(),
+                            v.astype(np.float64).tolist(), lq, lkv, hq, hkv,
+                            float(np.float32(0.7)), causal, softcap, window=window)
+    want = np.asarray(want, dtype=np.float64).reshape(tq * hq, dv)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lq,lkv,window", [(6, 6, 2), (3, 9, 4), (7, 4, 3), (1, 5, 2), (5, 1, 1), (8, 8, 8)])
+def test_identical_keys_give_window_mean(causal, lq, lkv, window):
+    """With identical keys every visible key weighs the same, so row i is the mean
+    of V over keys max(0, i+off+1-W) .. i+off (causal) or .. L_kv-1 (not causal),
+    off = L_kv - L_q: the window's left edge pinned exactly."""
+    d = 4
+    q = _rand((lq, 1, d))
+    k = np.repeat(_rand((1, 1, d)), lkv, axis=0)
+    v = _rand((lkv, 1, d))
+    got = _run(q, k, v, [lq], [lkv], 1, 1, 0.5, causal, 0.0, local_window=window)
+    off = lkv - lq
+    vd = v.astype(np.float64)[:, 0, :]
+    for i in range(lq):
+        lo = max(0, i + off + 1 - window)
+        hi = min(lkv, i + off + 1) if causal else lkv
+        want = np.zeros(d) if hi <= lo else vd[lo:hi].mean(axis=0)
+        np.testing.assert_allclose(got[i], want, rtol=0, atol=1e-14)
+
+
+def test_window_of_one_returns_the_diagonal_value():
+    """W = 1 with the causal mask leaves exactly key i + off: out = V of that key."""
+    lq, lkv = [5, 3], [7, 3]
+    q, k, v = _rand((8, 2, 4)), _rand((10, 1, 4)), _rand((10, 1, 4))
+    got = _run(q, k, v, lq, lkv, 2, 1, 0.9, True, 3.0, local_window=1).reshape(8, 2, 4)
+    rows = [(0, i, 7 - 5 + i) for i in range(5)] + [(1, i, i) for i in range(3)]
+    for t, (b, i, j) in enumerate(rows):
+        kt = j + (0 if b == 0 else 7)
+        for h in range(2):
+            np.testing.assert_array_equal(got[t, h], v[kt, 0].astype(np.float64))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_covering_every_key_changes_nothing(causal):
+    lq, lkv = [4, 6, 1], [9, 6, 5]
+    q, k, v = _rand((11, 4, 8)), _rand((20, 2, 8)), _rand((20, 2, 8))
+    base = _run(q, k, v, lq, lkv, 4, 2, 0.4, causal, 0.0)
+    for w in (9, 10, 1000):
+        np.testing.assert_array_equal(_run(q, k, v, lq, lkv, 4, 2, 0.4, causal, 0.0, local_window=w), base)
+    np.testing.assert_array_equal(_run(q, k, v, lq, lkv, 4, 2, 0.4, causal, 0.0, local_window=-1), base)
