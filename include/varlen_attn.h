@@ -123,10 +123,22 @@ varlen_status_t varlen_attn_fwd(const void* q, const void* k, const void* v,
                                 void* out, void* stream);
 
 /*
- * Options that steer how the work is split, for tests that prove the paths
- * agree and for tuning. Passing NULL options to varlen_attn_fwd_ex is the
- * same as varlen_attn_fwd. The result is the same for every option value up
- * to fp32 rounding.
+ * Extra arguments of varlen_attn_fwd_ex. Passing NULL (or a zeroed struct)
+ * is the same as varlen_attn_fwd.
+ *
+ *  local_window   the one field that changes the result: W > 0 keeps, for
+ *                 query row i of a sequence, only the keys
+ *                 j >= i + L_kv - L_q + 1 - W (the W keys that end at the
+ *                 row's tail-aligned diagonal), with or without is_causal
+ *                 (page src/kernels/attention.rs, softmax kernel source,
+ *                 local_min; page src/kernels/group_query_attention.rs,
+ *                 attribute local_window_size). 0 and -1 mean no window
+ *                 (-1 is that attribute's default; 0 is what a zeroed struct
+ *                 holds); below -1 returns VARLEN_ERR_INVALID_ARGUMENT.
+ *
+ * The other fields steer how the work is split, for tests that prove the
+ * paths agree and for tuning; the result is the same for every value of
+ * them up to fp32 rounding.
  *
  *  decode_path    0 auto (split-KV decode kernel for sequences with L_q == 1
  *                 on bf16/f16), 1 never (every sequence through the prefill
@@ -141,7 +153,8 @@ typedef struct {
   int32_t decode_path;
   int32_t decode_chunk;
   int32_t prefill_kv_chunk;
-  int32_t reserved[5];
+  int32_t local_window;
+  int32_t reserved[4];
 } varlen_attn_options_t;
 
 varlen_status_t varlen_attn_fwd_ex(const void* q, const void* k, const void* v,
@@ -207,6 +220,14 @@ varlen_status_t varlen_attn_plan(const int32_t* cu_seqlens_q_host,
 int64_t varlen_attn_valid_pairs(const int32_t* cu_seqlens_q_host,
                                 const int32_t* cu_seqlens_kv_host, int32_t batch,
                                 int32_t is_causal);
+
+/* The same count with a local window of local_window keys (<= 0: none): row i
+ * sees the keys j in [max(0, i + off + 1 - W), hi), off = L_kv - L_q, hi =
+ * clamp(i + off + 1, 0, L_kv) with is_causal and L_kv without. Returns -1 on
+ * invalid arrays. */
+int64_t varlen_attn_valid_pairs_window(const int32_t* cu_seqlens_q_host,
+                                       const int32_t* cu_seqlens_kv_host, int32_t batch,
+                                       int32_t is_causal, int32_t local_window);
 
 /*
  * Kernel timing for measurement tools (not needed for computing). While

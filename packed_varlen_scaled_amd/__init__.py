@@ -43,7 +43,8 @@ class VarlenAttnError(RuntimeError):
 
 class Options(ctypes.Structure):
     _fields_ = [("decode_path", ctypes.c_int32), ("decode_chunk", ctypes.c_int32),
-                ("prefill_kv_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("prefill_kv_chunk", ctypes.c_int32), ("local_window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 class PlanStats(ctypes.Structure):
@@ -88,6 +89,8 @@ def load_library():
     lib.varlen_attn_plan.restype = ctypes.c_int
     lib.varlen_attn_valid_pairs.argtypes = [vp, vp, i32, i32]
     lib.varlen_attn_valid_pairs.restype = ctypes.c_int64
+    lib.varlen_attn_valid_pairs_window.argtypes = [vp, vp, i32, i32, i32]
+    lib.varlen_attn_valid_pairs_window.restype = ctypes.c_int64
     lib.varlen_attn_last_error.argtypes = []
     lib.varlen_attn_last_error.restype = ctypes.c_char_p
     lib.varlen_attn_release.argtypes = []
@@ -108,9 +111,10 @@ def _check(status: int):
         raise VarlenAttnError(status, msg)
 
 
-def _options(decode_path=0, decode_chunk=0, prefill_kv_chunk=0):
+def _options(decode_path=0, decode_chunk=0, prefill_kv_chunk=0, local_window=None):
     o = Options()
     o.decode_path, o.decode_chunk, o.prefill_kv_chunk = int(decode_path), int(decode_chunk), int(prefill_kv_chunk)
+    o.local_window = -1 if local_window is None else int(local_window)
     return o
 
 
@@ -153,12 +157,15 @@ def _host_cu(x):
 def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None,
                     scale=None, is_causal: bool = False, softcap: float = 0.0, out=None,
                     cu_seqlens_q_host=None, cu_seqlens_kv_host=None, stream=None,
-                    decode_path: int = 0, decode_chunk: int = 0, prefill_kv_chunk: int = 0):
+                    decode_path: int = 0, decode_chunk: int = 0, prefill_kv_chunk: int = 0,
+                    local_window=None):
     """Packed varlen attention forward on the current GPU stream.
 
     q, k, v: CUDA(HIP) tensors, rank 3 ``[T, H, D]`` or rank 2 ``[T, H*D]``.
     cu_seqlens_q / cu_seqlens_kv: int32 CUDA tensors ``[B+1]``; the optional
     host mirrors (any int sequence) spare the library a device->host read.
+    local_window: None or -1 for no window; W > 0 keeps for row i only the
+    keys j >= i + L_kv - L_q + 1 - W.
     Returns ``out`` (allocated like q with v's head size when not given)."""
     import torch
     lib = load_library()
@@ -196,7 +203,7 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num
     hkv_host = _host_cu(cu_seqlens_kv_host)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    opts = _options(decode_path, decode_chunk, prefill_kv_chunk)
+    opts = _options(decode_path, decode_chunk, prefill_kv_chunk, local_window)
     with torch.cuda.device(q.device):
         st = lib.varlen_attn_fwd_ex(
             q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -214,7 +221,7 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num
 def plan(cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None, head_dim: int = 128,
          v_head_dim: int = 0, dtype: str = "bf16", scale: float = 0.0, is_causal: bool = False,
          softcap: float = 0.0, with_items: bool = False, decode_path: int = 0, decode_chunk: int = 0,
-         prefill_kv_chunk: int = 0):
+         prefill_kv_chunk: int = 0, local_window=None):
     """Run the host scheduler alone (no GPU needed). Returns (stats dict, items or None);
     items is an int32 array [n_items, 16] (see varlen_attn_plan in the header)."""
     import numpy as np
@@ -223,7 +230,7 @@ def plan(cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None, head_di
     if cq.size != ckv.size:
         raise ValueError("cu_seqlens_q and cu_seqlens_kv lengths differ")
     stats = PlanStats()
-    opts = _options(decode_path, decode_chunk, prefill_kv_chunk)
+    opts = _options(decode_path, decode_chunk, prefill_kv_chunk, local_window)
     args = (cq.ctypes.data, ckv.ctypes.data, cq.size - 1, int(cq[-1]) if cq.size else 0,
             int(ckv[-1]) if ckv.size else 0, int(num_heads), int(kv_num_heads or 0), int(head_dim),
             int(v_head_dim), DTYPE_CODES[dtype], float(scale), 1 if is_causal else 0, float(softcap),
@@ -238,11 +245,15 @@ def plan(cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None, head_di
     return stats.as_dict(), items
 
 
-def valid_pairs(cu_seqlens_q, cu_seqlens_kv, is_causal: bool) -> int:
+def valid_pairs(cu_seqlens_q, cu_seqlens_kv, is_causal: bool, local_window=None) -> int:
     """Visible (query row, key) pairs; attention FLOPs are 4 * pairs * Hq * D."""
     lib = load_library()
     cq, ckv = _host_cu(cu_seqlens_q), _host_cu(cu_seqlens_kv)
-    r = lib.varlen_attn_valid_pairs(cq.ctypes.data, ckv.ctypes.data, cq.size - 1, 1 if is_causal else 0)
+    if local_window is None:
+        r = lib.varlen_attn_valid_pairs(cq.ctypes.data, ckv.ctypes.data, cq.size - 1, 1 if is_causal else 0)
+    else:
+        r = lib.varlen_attn_valid_pairs_window(cq.ctypes.data, ckv.ctypes.data, cq.size - 1,
+                                               1 if is_causal else 0, int(local_window))
     if r < 0:
         raise ValueError("invalid cu_seqlens arrays")
     return int(r)

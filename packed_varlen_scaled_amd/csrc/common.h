@@ -58,6 +58,7 @@ struct Params {
   float* part_lse;
   int32_t hq, hkv, group, d, dv;
   int32_t causal;
+  int32_t window;  // > 0: row i sees only keys j >= i + L_kv - L_q + 1 - window
   int32_t softcap_on;
   // Scores are worked in log2 units: y = s * score_log2 without softcap, and
   // y = cap_log2 * tanh(s * scale / |softcap|) with it, where the tanh is

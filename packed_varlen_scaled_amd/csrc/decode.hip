@@ -133,7 +133,8 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
     const int kcur = kb;
     if (kb + NW * BK < kv_end) load_block(kb + NW * BK);
     // sacc[mt][r]: head slot n, key kcur + 16*mt + 4*grp + r.
-    const bool need_mask = (kcur + BK > kv_end) || (p.causal && kcur + BK - 1 > i_local + off);
+    const bool need_mask = (kcur + BK > kv_end) || (p.causal && kcur + BK - 1 > i_local + off) ||
+                           (p.window > 0 && kcur < i_local + off + 1 - p.window);
     float mx = ninf();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -142,7 +143,8 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
         float s = sacc[mt][r];
         if (need_mask) {
           const int key = kcur + 16 * mt + 4 * grp + r;
-          const bool bad = key >= kv_end || (p.causal && key > i_local + off);
+          const bool bad = key >= kv_end || (p.causal && key > i_local + off) ||
+                           (p.window > 0 && key < i_local + off + 1 - p.window);
           s = bad ? ninf() : s;
           sacc[mt][r] = s;
         }

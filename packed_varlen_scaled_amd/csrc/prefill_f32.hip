@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(Params p, const WorkIt
       acc *= p.scale;
       if (p.softcap_on) acc = p.softcap * tanhf(acc / p.softcap);
       const int j = kt + key;
-      const bool bad = j >= it.kv_end || (p.causal && j > i_local + off);
+      const bool bad = j >= it.kv_end || (p.causal && j > i_local + off) ||
+                       (p.window > 0 && j < i_local + off + 1 - p.window);
       s[u] = bad ? ninf() : acc;
       mx = fmaxf(mx, s[u]);
     }

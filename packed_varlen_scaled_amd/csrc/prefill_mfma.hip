@@ -39,6 +39,7 @@
 // Rows of the tile that lie past the sequence are never stored; keys at or
 // past kv_end are zero-filled in LDS (so data of the next sequence can never
 // reach a product) and masked.
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -96,6 +97,10 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const bool wave_active = row0 < it.q_rows;
   const int wave_first = it.q_row_begin + row0;
   const int wave_last = it.q_row_begin + min(row0 + 31, it.q_rows - 1);
+  // Keys this lane's row may see: [key_lo, key_hi] (tail-aligned causal
+  // bound, local window of p.window keys ending at the diagonal, kv_end).
+  const int key_hi = p.causal ? min(it.kv_end - 1, i_local + off) : it.kv_end - 1;
+  const int key_lo = p.window > 0 ? i_local + off + 1 - p.window : INT_MIN;
   const int kv_begin = it.kv_begin;
   const int kv_end = it.kv_end;
   const int64_t tok = (int64_t)it.q_token0 + it.q_row_begin + my_row;
@@ -182,7 +187,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   //   kFirst  - first tile of the item: masked; sets each row's reference
   //             max m_ref, against which every later P is taken;
   //   kPlain  - a tile that needs no mask for any row of the workgroup;
-  //   kMasked - a tile that crosses the causal frontier or kv_end;
+  //   kMasked - a tile that crosses the causal frontier, a window edge or
+  //             kv_end;
   //   kSafe   - the textbook online softmax (masked, running max, O rescaled
   //             on every tile), used only to redo an item whose P, l or O
   //             overflowed against the first tile's max.
@@ -226,7 +232,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool bad = key >= kv_end || (p.causal && key > i_local + off);
+          const bool bad = key > key_hi || key < key_lo;
           sacc[mt][r] = bad ? ninf() : sacc[mt][r];
         }
       }
@@ -255,6 +261,30 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
         l_run *= alpha;
 #pragma unroll
         for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+      }
+    }
+    if constexpr (MODE == kPlain || MODE == kMasked) {
+      // A row whose first visible key lies past the first tile (rows of a
+      // later 32-row block under a local window) still has no reference
+      // max: it takes this tile's. Its O and l are still zero, so nothing
+      // needs rescaling. Rows that see no key at all keep -inf.
+      if (__builtin_expect(__any(m_ref == ninf()), 0)) {
+        asm volatile("" ::: "memory");
+        float mx = ninf();
+#pragma unroll
+        for (int mt = 0; mt < BN / 32; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sacc[mt][r]), sacc[mt][r + 1]);
+        }
+        mx = max_with_partner32(mx);
+        float tmax;
+        if constexpr (SOFTCAP) {
+          tmax = (mx == ninf()) ? ninf()
+                                : p.cap_log2 * (1.f - 2.f * rcp_fast(exp2_fast(mx * p.tanh_log2) + 1.f));
+        } else {
+          tmax = mx * p.score_log2;
+        }
+        m_ref = (m_ref == ninf()) ? tmax : m_ref;
       }
     }
     const float m_use = (m_ref == ninf()) ? 0.f : m_ref;
@@ -316,18 +346,24 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   // barrier (all waves' loads landed; the other buffer is free again), start
   // loading the next tile into the other buffer, compute the current one.
   const int n_tiles = (kv_end - kv_begin + BN - 1) / BN;
-  // Tiles [1, n_plain) need no mask for any row of the workgroup: they end at
-  // or before kv_end and before the first row's causal frontier.
-  int n_plain = n_tiles;
-  {
-    const int lim_end = (kv_end - kv_begin) / BN;  // full tiles
-    n_plain = min(n_plain, lim_end);
-    if (p.causal) {
-      const int frontier = it.q_row_begin + off + 1;  // keys [0, frontier) seen by every row
-      n_plain = min(n_plain, max(0, (frontier - kv_begin) / BN));
-    }
-    n_plain = max(n_plain, 1);
+  // Tiles [t_plain0, t_plain1) need no mask for any row of the workgroup:
+  // they end at or before kv_end, before the first row's causal frontier and
+  // start at or after the last row's window start.
+  int t_plain1 = (kv_end - kv_begin) / BN;  // full tiles
+  if (p.causal) {
+    const int frontier = it.q_row_begin + off + 1;  // keys [0, frontier) seen by every row
+    t_plain1 = min(t_plain1, max(0, (frontier - kv_begin) / BN));
   }
+  int t_plain0 = 1;
+  if (p.window > 0) {
+    const int lo_last = it.q_row_begin + it.q_rows - 1 + off + 1 - p.window;  // last row's window start
+    t_plain0 = max(1, (lo_last - kv_begin + BN - 1) / BN);
+  }
+  // This wave's rows see none of the keys of the tile at kt.
+  auto skips = [&](int kt) {
+    return !wave_active || (p.causal && kt > wave_last + off) ||
+           (p.window > 0 && kt + BN <= wave_first + off + 1 - p.window);
+  };
   auto step = [&](int t) {
     const int kt = kv_begin + t * BN;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t have landed
@@ -341,14 +377,21 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     if constexpr (SAFE) {
       for (int t = 0; t < n_tiles; ++t) {
         const int kt = step(t);
-        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kSafe>{});
+        if (!skips(kt)) compute(t & 1, kt, std::integral_constant<int, kSafe>{});
       }
     } else {
+      // regions: first tile | masked (left window edge) | plain | masked
       if (n_tiles > 0) compute(0, step(0), std::integral_constant<int, kFirst>{});
-      for (int t = 1; t < n_plain; ++t) compute(t & 1, step(t), std::integral_constant<int, kPlain>{});
-      for (int t = max(n_plain, 1); t < n_tiles; ++t) {
+      const int p0 = min(t_plain0, n_tiles);
+      const int p1 = max(p0, min(t_plain1, n_tiles));
+      for (int t = 1; t < p0; ++t) {
         const int kt = step(t);
-        if (wave_active && !(p.causal && kt > wave_last + off)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
+        if (!skips(kt)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
+      }
+      for (int t = p0; t < p1; ++t) compute(t & 1, step(t), std::integral_constant<int, kPlain>{});
+      for (int t = max(p1, 1); t < n_tiles; ++t) {
+        const int kt = step(t);
+        if (!skips(kt)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
       }
     }
   };

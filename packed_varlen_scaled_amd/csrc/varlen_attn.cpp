@@ -54,6 +54,7 @@ struct Problem {
   int32_t hq, hkv, group, d, dv, dtype;
   float scale;  // effective scale
   int32_t causal;
+  int32_t window;  // 0: none; > 0: keys j >= i + off + 1 - window
   float softcap;
   const int32_t* cu_q;   // host
   const int32_t* cu_kv;  // host
@@ -63,6 +64,7 @@ struct Options {
   int32_t decode_path = 0;
   int32_t decode_chunk = 0;
   int32_t prefill_kv_chunk = 0;
+  int32_t local_window = 0;
 };
 
 Options resolve_options(const varlen_attn_options_t* o) {
@@ -71,8 +73,19 @@ Options resolve_options(const varlen_attn_options_t* o) {
     r.decode_path = o->decode_path;
     r.decode_chunk = o->decode_chunk;
     r.prefill_kv_chunk = o->prefill_kv_chunk;
+    r.local_window = o->local_window;
   }
   return r;
+}
+
+// The local window: -1 (the GroupQueryAttention attribute's default) and 0
+// mean none; below -1 is rejected as that op rejects it (page
+// src/kernels/group_query_attention.rs, local_window_size validation).
+varlen_status_t check_window(int32_t w, Problem* pr) {
+  if (w < -1)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "local_window must be -1 or 0 (no window) or a positive key count, got %d", w);
+  pr->window = w > 0 ? w : 0;
+  return VARLEN_OK;
 }
 
 // Scalar and shape checks that need no cu arrays.
@@ -154,17 +167,26 @@ struct Plan {
   int32_t heads_per_item = 0;
 };
 
-int64_t valid_pairs_of(const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, bool causal) {
+int64_t valid_pairs_of(const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, bool causal, int32_t window) {
   int64_t total = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t lq = (int64_t)cu_q[b + 1] - cu_q[b];
     const int64_t lkv = (int64_t)cu_kv[b + 1] - cu_kv[b];
+    const int64_t off = lkv - lq;
+    if (window > 0) {
+      // row i sees [clamp(i + off + 1 - W, 0, lkv), hi)
+      for (int64_t i = 0; i < lq; ++i) {
+        const int64_t hi = causal ? std::min(lkv, std::max<int64_t>(0, i + off + 1)) : lkv;
+        const int64_t lo = std::min(lkv, std::max<int64_t>(0, i + off + 1 - window));
+        total += std::max<int64_t>(0, hi - lo);
+      }
+      continue;
+    }
     if (!causal) {
       total += lq * lkv;
       continue;
     }
-    // row i sees clamp(i + off + 1, 0, lkv) keys, off = lkv - lq
-    const int64_t off = lkv - lq;
+    // row i sees clamp(i + off + 1, 0, lkv) keys
     const int64_t i_first = std::max<int64_t>(0, -off);          // first row seeing >= 1 key
     const int64_t i_full = std::max<int64_t>(0, lkv - off - 1);  // first row seeing all keys
     const int64_t lo = std::min(lq, i_first);
@@ -191,12 +213,19 @@ WorkItem make_item(int32_t kind, int32_t b, const Problem& pr) {
   return it;
 }
 
-// Keys [0, kv_end) that rows [r0, r0 + rows) of a sequence can see.
+// Keys [visible_begin, visible_end) that rows [r0, r0 + rows) of a sequence
+// can see: the union of the rows' ranges (consecutive rows see overlapping,
+// shifting ranges). An empty range (begin >= end) means the rows see nothing.
 int32_t visible_end(const WorkItem& it, int32_t r0, int32_t rows, bool causal) {
   if (!causal) return it.len_kv;
   const int64_t last = (int64_t)r0 + rows - 1;
   const int64_t e = last + (it.len_kv - it.len_q) + 1;
   return (int32_t)std::min<int64_t>(it.len_kv, std::max<int64_t>(0, e));
+}
+int32_t visible_begin(const WorkItem& it, int32_t r0, int32_t window) {
+  if (window <= 0) return 0;
+  const int64_t b = (int64_t)r0 + (it.len_kv - it.len_q) + 1 - window;
+  return (int32_t)std::min<int64_t>(it.len_kv, std::max<int64_t>(0, b));
 }
 
 int largest_pow2_divisor_upto(int g, int cap) {
@@ -212,10 +241,13 @@ int largest_pow2_divisor_upto(int g, int cap) {
 
 // Splits tile items (all with the same rows and heads) over [kv_begin, kv_end)
 // in chunks; appends them (and their combine item) to `dst`/`plan.combine`.
-void emit_split(Plan& plan, std::vector<WorkItem>& dst, WorkItem base, int32_t kv_end, int32_t chunk) {
-  const int32_t n_splits = std::max<int32_t>(1, (kv_end + chunk - 1) / chunk);
+// An empty range gives one item with no keys (it writes zero rows).
+void emit_split(Plan& plan, std::vector<WorkItem>& dst, WorkItem base, int32_t kv_begin, int32_t kv_end,
+                int32_t chunk) {
+  kv_end = std::max(kv_begin, kv_end);
+  const int32_t n_splits = std::max<int32_t>(1, (kv_end - kv_begin + chunk - 1) / chunk);
   if (n_splits == 1) {
-    base.kv_begin = 0;
+    base.kv_begin = kv_begin;
     base.kv_end = kv_end;
     dst.push_back(base);
     return;
@@ -226,20 +258,20 @@ void emit_split(Plan& plan, std::vector<WorkItem>& dst, WorkItem base, int32_t k
   for (int32_t s = 0; s < n_splits; ++s) {
     WorkItem it = base;
     it.split = s;
-    it.kv_begin = s * chunk;
-    it.kv_end = std::min(kv_end, (s + 1) * chunk);
+    it.kv_begin = kv_begin + s * chunk;
+    it.kv_end = std::min(kv_end, kv_begin + (s + 1) * chunk);
     dst.push_back(it);
   }
   WorkItem c = base;
   c.kind = pva::kCombine;
-  c.kv_begin = 0;
+  c.kv_begin = kv_begin;
   c.kv_end = kv_end;
   plan.combine.push_back(c);
 }
 
 varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
   const bool causal = pr.causal != 0;
-  plan.valid_pairs = valid_pairs_of(pr.cu_q, pr.cu_kv, pr.batch, causal);
+  plan.valid_pairs = valid_pairs_of(pr.cu_q, pr.cu_kv, pr.batch, causal, pr.window);
   if (pr.dtype == VARLEN_F32) {
     plan.prefill_waves = 4;
     plan.heads_per_item = 1;
@@ -247,17 +279,18 @@ varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
       const WorkItem proto = make_item(pva::kPrefillF32, b, pr);
       for (int32_t r0 = 0; r0 < proto.len_q; r0 += 32) {
         const int32_t rows = std::min(32, proto.len_q - r0);
-        const int32_t kv_end = visible_end(proto, r0, rows, causal);
+        const int32_t kv_begin = visible_begin(proto, r0, pr.window);
+        const int32_t kv_end = std::max(kv_begin, visible_end(proto, r0, rows, causal));
         for (int32_t h = 0; h < pr.hq; ++h) {
           WorkItem it = proto;
           it.q_row_begin = r0;
           it.q_rows = rows;
           it.head_begin = h;
           it.heads = 1;
-          it.kv_begin = 0;
+          it.kv_begin = kv_begin;
           it.kv_end = kv_end;
           plan.f32.push_back(it);
-          plan.visited_pairs_x_heads += (int64_t)rows * kv_end;
+          plan.visited_pairs_x_heads += (int64_t)rows * (kv_end - kv_begin);
         }
       }
     }
@@ -299,23 +332,26 @@ varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
           it.q_rows = 1;
           it.head_begin = h0;
           it.heads = nh_dec;
-          const int32_t kv_end = visible_end(proto, 0, 1, causal);
-          emit_split(plan, plan.decode, it, kv_end, dchunk);
-          plan.visited_pairs_x_heads += (int64_t)kv_end * nh_dec;
+          const int32_t kv_begin = visible_begin(proto, 0, pr.window);
+          const int32_t kv_end = std::max(kv_begin, visible_end(proto, 0, 1, causal));
+          emit_split(plan, plan.decode, it, kv_begin, kv_end, dchunk);
+          plan.visited_pairs_x_heads += (int64_t)(kv_end - kv_begin) * nh_dec;
         }
         continue;
       }
       for (int32_t r0 = 0; r0 < proto.len_q; r0 += rows_per_item) {
         const int32_t rows = std::min(rows_per_item, proto.len_q - r0);
-        const int32_t kv_end = visible_end(proto, r0, rows, causal);
+        const int32_t kv_begin = visible_begin(proto, r0, pr.window);
+        const int32_t kv_end = std::max(kv_begin, visible_end(proto, r0, rows, causal));
         for (int32_t h0 = 0; h0 < pr.hq; h0 += nh) {
           WorkItem it = proto;
           it.q_row_begin = r0;
           it.q_rows = rows;
           it.head_begin = h0;
           it.heads = nh;
-          emit_split(plan, plan.prefill, it, kv_end, pchunk > 0 ? pchunk : std::max<int32_t>(kv_end, 1));
-          plan.visited_pairs_x_heads += (int64_t)rows * kv_end * nh;
+          emit_split(plan, plan.prefill, it, kv_begin, kv_end,
+                     pchunk > 0 ? pchunk : std::max<int32_t>(kv_end - kv_begin, 1));
+          plan.visited_pairs_x_heads += (int64_t)rows * (kv_end - kv_begin) * nh;
         }
       }
     }
@@ -443,6 +479,7 @@ varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* 
                                      dtype, scale, softcap, &pr);
   if (st != VARLEN_OK) return st;
   pr.causal = is_causal != 0;
+  if ((st = check_window(options ? options->local_window : 0, &pr)) != VARLEN_OK) return st;
   if (total_q > 0 && (!q || !out))
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "query and output pointers must be non-null");
   if (total_kv > 0 && (!k || !v))
@@ -552,6 +589,7 @@ varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* 
   p.d = pr.d;
   p.dv = pr.dv;
   p.causal = pr.causal;
+  p.window = pr.window;
   p.softcap_on = pr.softcap != 0.f;
   const float log2e = 1.4426950408889634f;
   p.scale = pr.scale;
@@ -617,6 +655,7 @@ varlen_status_t varlen_attn_plan(const int32_t* cu_seqlens_q_host, const int32_t
                                      dtype, scale, softcap, &pr);
   if (st != VARLEN_OK) return st;
   pr.causal = is_causal != 0;
+  if ((st = check_window(options ? options->local_window : 0, &pr)) != VARLEN_OK) return st;
   if (!cu_seqlens_q_host || !cu_seqlens_kv_host)
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "varlen_attn_plan needs host cu arrays");
   if ((st = check_cu(cu_seqlens_q_host, batch, total_q, "cu_seqlens_q")) != VARLEN_OK) return st;
@@ -664,7 +703,13 @@ int64_t varlen_attn_valid_pairs(const int32_t* cu_seqlens_q_host, const int32_t*
       return -1;
   }
   if (cu_seqlens_q_host[0] != 0 || cu_seqlens_kv_host[0] != 0) return -1;
-  return valid_pairs_of(cu_seqlens_q_host, cu_seqlens_kv_host, batch, is_causal != 0);
+  return valid_pairs_of(cu_seqlens_q_host, cu_seqlens_kv_host, batch, is_causal != 0, 0);
+}
+
+int64_t varlen_attn_valid_pairs_window(const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_kv_host,
+                                       int32_t batch, int32_t is_causal, int32_t local_window) {
+  if (varlen_attn_valid_pairs(cu_seqlens_q_host, cu_seqlens_kv_host, batch, is_causal) < 0) return -1;
+  return valid_pairs_of(cu_seqlens_q_host, cu_seqlens_kv_host, batch, is_causal != 0, local_window);
 }
 
 const char* varlen_attn_last_error(void) { return g_last_error.c_str(); }

@@ -30,11 +30,11 @@ def run_gpu(batch: synth.Batch, out=None, **opts):
     return o
 
 
-def oracle_all(batch: synth.Batch, threads: int = 0):
+def oracle_all(batch: synth.Batch, threads: int = 0, local_window: int = 0):
     w = batch.workload
     out = oracle.attention(batch.q.cpu(), batch.k.cpu(), batch.v.cpu(), batch.cu_q, batch.cu_kv,
                            w.num_heads, w.kv_num_heads, scale=w.scale or None, is_causal=w.is_causal,
-                           softcap=w.softcap, dtype=w.dtype, threads=threads)
+                           softcap=w.softcap, dtype=w.dtype, threads=threads, local_window=local_window)
     return out.reshape(batch.total_q, w.num_heads, w.dv)
 
 
@@ -56,7 +56,7 @@ def sample_rows(batch: synth.Batch, seqs, rows_per_seq: int, seed: int = 0):
     return picks
 
 
-def oracle_sampled(batch: synth.Batch, picks, threads: int = 0):
+def oracle_sampled(batch: synth.Batch, picks, threads: int = 0, local_window: int = 0):
     """Oracle values for (seq, row, head) picks, computed on a sub-batch made of
     just the picked sequences (so no full-size K/V ever goes to the host)."""
     w = batch.workload
@@ -77,7 +77,7 @@ def oracle_sampled(batch: synth.Batch, picks, threads: int = 0):
     rows = np.array([(int(cq[pos[b]]) + r) * w.num_heads + h for b, r, h in picks], dtype=np.int64)
     return oracle.attention(q, k, v, cq, ckv, w.num_heads, w.kv_num_heads, scale=w.scale or None,
                             is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, rows=rows,
-                            threads=threads)
+                            threads=threads, local_window=local_window)
 
 
 def gather_gpu(batch: synth.Batch, out, picks):

@@ -267,3 +267,59 @@ def test_back_to_back_calls_on_two_streams():
     for r in range(4):
         for i in range(3):
             assert torch.equal(outs[r][i], alone[i]), (r, i)
+
+
+# Local window (page src/kernels/attention.rs, softmax kernel local_min; page
+# src/kernels/group_query_attention.rs, local_window_size): each case against
+# the oracle with the same window.
+WINDOW = [
+    # (name, workload kwargs, lq, lkv, window, options)
+    ("bf16_gqa4_causal_w48", dict(hq=8, hkv=2), [70, 1, 129, 33, 0, 200], [70, 1, 129, 33, 5, 200], 48, {}),
+    ("bf16_gqa4_causal_w1", dict(hq=8, hkv=2), [70, 9], [70, 40], 1, {}),
+    ("bf16_gqa4_tail_aligned_w100", dict(hq=8, hkv=2), [40, 3, 100, 1], [300, 90, 100, 17], 100, {}),
+    ("bf16_noncausal_w70", dict(hq=4, hkv=4, causal=False), [77, 128, 5], [31, 128, 200], 70, {}),
+    ("bf16_mha_rows4_w20", dict(hq=2, hkv=2), [300, 77], [300, 77], 20, {}),
+    ("bf16_gqa2_rows2_w150", dict(hq=4, hkv=2), [257, 64], [257, 400], 150, {}),
+    ("bf16_gqa8_softcap_w64", dict(hq=16, hkv=2, softcap=30.0, sigma=1.5), [150, 64, 1], [150, 64, 900], 64, {}),
+    ("f16_gqa4_w33", dict(dtype="f16", hq=8, hkv=2), [70, 1, 129], [70, 700, 129], 33, {}),
+    ("bf16_d64_w10", dict(hq=8, hkv=2, d=64), [100, 1, 37], [100, 513, 37], 10, {}),
+    ("bf16_lq_gt_lkv_w5", dict(hq=4, hkv=1), [50, 65], [10, 64], 5, {}),
+    ("bf16_window_covers_all", dict(hq=8, hkv=2), [90, 2], [90, 70], 100000, {}),
+    ("bf16_decode_split_w700", dict(hq=16, hkv=2), [1, 1, 1, 100], [3000, 500, 800, 1000], 700,
+     dict(decode_chunk=256)),
+    ("bf16_prefill_split_w300", dict(hq=8, hkv=2, softcap=20.0), [257, 100], [900, 1000], 300,
+     dict(prefill_kv_chunk=128)),
+    ("bf16_prefill_only_w90", dict(hq=8, hkv=2), [1, 64, 1], [500, 64, 91], 90, dict(decode_path=1)),
+    ("f32_gqa_w7", dict(dtype="f32", hq=8, hkv=2, d=64), [70, 1, 33], [70, 200, 40], 7, {}),
+    ("f32_noncausal_w12", dict(dtype="f32", hq=4, hkv=4, d=128, softcap=5.0, causal=False), [40, 3], [17, 90], 12, {}),
+]
+
+
+@pytest.mark.parametrize("name,kw,lq,lkv,window,opts", WINDOW, ids=[c[0] for c in WINDOW])
+def test_local_window_matches_oracle(name, kw, lq, lkv, window, opts):
+    w = _workload(**kw)
+    _say(name, w, lq, lkv, "window", window, opts)
+    batch = _batch(w, lq, lkv)
+    got = run_gpu(batch, local_window=window, **opts).double().cpu().numpy().reshape(
+        batch.total_q, w.num_heads, w.dv)
+    ma, rel = compare(got, oracle_all(batch, local_window=window), w.dtype)
+    _say(name, "max_abs", ma, "rel_l2", rel)
+
+
+def test_local_window_full_size_sampled():
+    """The long causal softcap workload with a 4096-key window, launched as the
+    benchmark's --window run launches it; sampled rows against the oracle."""
+    import torch
+    name, window = "long_causal_softcap", 4096
+    w = synth.WORKLOADS[name]
+    _say("full window", name, window)
+    batch = synth.workload_batch(name, device="cuda")
+    out = run_gpu(batch, local_window=window)
+    longest = int(np.argmax(np.asarray(batch.lkv)))
+    seqs = sorted({0, longest, len(batch.lq) - 1})
+    picks = sample_rows(batch, seqs, rows_per_seq=6)
+    ma, rel = compare(gather_gpu(batch, out, picks), oracle_sampled(batch, picks, local_window=window), w.dtype)
+    _say("full window", name, len(picks), "rows max_abs", ma, "rel_l2", rel)
+    assert torch.isfinite(out.float()).all()
+    del batch, out
+    torch.cuda.empty_cache()

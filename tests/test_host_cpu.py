@@ -105,14 +105,45 @@ def test_empty_query_batch_is_ok_without_device_work():
 # --------------------------------------------------------------------------
 # Valid-pair count.
 # --------------------------------------------------------------------------
-def _brute_pairs(lq, lkv, causal):
+def _brute_pairs(lq, lkv, causal, window=0):
     n = 0
     for a, b in zip(lq, lkv):
         for i in range(a):
             for j in range(b):
-                if not causal or j <= i + b - a:
+                if (not causal or j <= i + b - a) and (window <= 0 or j >= i + b - a + 1 - window):
                     n += 1
     return n
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [1, 3, 17])
+def test_valid_pairs_with_window_matches_brute_force(causal, window):
+    rng = np.random.default_rng(6 + window)
+    for _ in range(40):
+        bsz = int(rng.integers(1, 6))
+        lq = rng.integers(0, 40, size=bsz).tolist()
+        lkv = rng.integers(0, 40, size=bsz).tolist()
+        assert pva.valid_pairs(_cu(lq), _cu(lkv), causal, local_window=window) == \
+            _brute_pairs(lq, lkv, causal, window)
+
+
+def test_window_argument_validation():
+    lib = pva.load_library()
+    cq, ck = _cu([3, 4]), _cu([5, 2])
+    for w, ok in [(-2, False), (-100, False), (-1, True), (0, True), (1, True), (1 << 20, True)]:
+        opts = pva.Options()
+        opts.local_window = w
+        st = lib.varlen_attn_plan(cq.ctypes.data, ck.ctypes.data, 2, 7, 7, 4, 2, 64, 0, 2, 0.0, 1, 0.0,
+                                  ctypes.byref(opts), ctypes.byref(pva.PlanStats()), None, 0)
+        msg = lib.varlen_attn_last_error().decode()
+        assert (st == 0) == ok, (w, st, msg)
+        if not ok:
+            assert st == 1 and "local_window" in msg, msg
+        fake = ctypes.c_void_p(1)
+        st = lib.varlen_attn_fwd_ex(fake, fake, fake, None, None, cq.ctypes.data, ck.ctypes.data, 2, 7, 7, 4, 2,
+                                    64, 0, 2, 0.0, 1, 0.0, None if ok else fake, None, ctypes.byref(opts))
+        if not ok:
+            assert st == 1 and "local_window" in lib.varlen_attn_last_error().decode()
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -131,9 +162,9 @@ def test_valid_pairs_matches_brute_force(causal):
 KIND_PREFILL, KIND_F32, KIND_DECODE, KIND_COMBINE = 0, 1, 2, 3
 
 
-def _coverage(lq, lkv, hq, hkv, causal, dtype="bf16", d=128, **opts):
+def _coverage(lq, lkv, hq, hkv, causal, dtype="bf16", d=128, window=0, **opts):
     stats, items = pva.plan(_cu(lq), _cu(lkv), hq, hkv, head_dim=d, dtype=dtype, is_causal=causal,
-                            with_items=True, **opts)
+                            with_items=True, local_window=window or None, **opts)
     cq, ck = _cu(lq), _cu(lkv)
     # visits[(token, head)] -> list of key index arrays
     visits = {}
@@ -160,7 +191,9 @@ def _coverage(lq, lkv, hq, hkv, causal, dtype="bf16", d=128, **opts):
                 key = (cq[b] + i, h)
                 got = np.concatenate(visits.get(key, [np.zeros(0, int)]))
                 # every visible key visited exactly once
-                visible = np.arange(lkv[b]) if not causal else np.arange(max(0, min(lkv[b], i + off + 1)))
+                hi = lkv[b] if not causal else max(0, min(lkv[b], i + off + 1))
+                lo = max(0, i + off + 1 - window) if window > 0 else 0
+                visible = np.arange(lo, max(lo, hi))
                 cnt = np.bincount(got, minlength=max(lkv[b], 1)) if got.size else np.zeros(max(lkv[b], 1), int)
                 assert np.all(cnt[visible] == 1), (b, i, h)
                 assert cnt.sum() - cnt[visible].sum() >= 0
@@ -177,6 +210,29 @@ def test_scheduler_covers_each_visible_pair_once(causal, hq, hkv):
     stats, _ = _coverage(lq, lkv, hq, hkv, causal)
     assert stats["valid_pairs"] == _brute_pairs(lq, lkv, causal)
     assert stats["visited_pairs"] >= stats["valid_pairs"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [1, 40, 150])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (64, 8), (4, 2), (3, 3)])
+def test_scheduler_with_window_covers_each_visible_pair_once(causal, window, hq, hkv):
+    lq = [1, 33, 70, 0, 5, 129, 1, 300]
+    lkv = [700, 33, 150, 4, 0, 100, 90, 300]
+    stats, items = _coverage(lq, lkv, hq, hkv, causal, window=window)
+    assert stats["valid_pairs"] == _brute_pairs(lq, lkv, causal, window)
+    # window-aware tile skipping: no item starts before the first key its first row can see
+    for it in items:
+        kind, seq, r0 = it[0], it[1], it[2]
+        if kind == KIND_COMBINE:
+            continue
+        off = lkv[seq] - lq[seq]
+        assert it[6] >= min(lkv[seq], max(0, r0 + off + 1 - window))
+    assert stats["visited_pairs"] <= 2 * stats["valid_pairs"] + 64 * 32 * len(items)
+
+
+@pytest.mark.parametrize("opts", [dict(decode_chunk=128), dict(prefill_kv_chunk=64)])
+def test_scheduler_splits_with_window_keep_coverage(opts):
+    _coverage([1, 40, 200, 1, 3], [700, 300, 200, 65, 1000], 32, 8, True, window=100, **opts)
 
 
 @pytest.mark.parametrize("opts", [dict(decode_path=1), dict(decode_chunk=128), dict(prefill_kv_chunk=64),
