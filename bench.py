@@ -44,12 +44,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def row_keys(lq, lkv, causal):
+def row_keys(lq, lkv, causal, window=0):
     """Visible keys of every query row, sequence by sequence (measurement only)."""
     out = []
     for a, b in zip(lq, lkv):
         i = np.arange(a, dtype=np.int64)
-        out.append(np.clip(i + (b - a) + 1, 0, b) if causal else np.full(a, b, dtype=np.int64))
+        hi = np.clip(i + (b - a) + 1, 0, b) if causal else np.full(a, b, dtype=np.int64)
+        lo = np.clip(i + (b - a) + 1 - window, 0, b) if window > 0 else np.zeros(a, dtype=np.int64)
+        out.append(np.maximum(hi - lo, 0))
     return out
 
 
@@ -90,7 +92,7 @@ def sub_batch(batch, seqs):
     return torch.cat(qs), torch.cat(ks), torch.cat(vs), synth.cu_seqlens(lq), synth.cu_seqlens(lkv), lq, lkv
 
 
-def cpu_baseline(batch, decode: bool, budget_s: float = 12.0):
+def cpu_baseline(batch, decode: bool, budget_s: float = 12.0, window: int = 0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the batch."""
     import oracle
     w = batch.workload
@@ -105,7 +107,8 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0):
             q, k, v, cq, ckv, lq, lkv = sub_batch(batch, take)
             t0 = time.perf_counter()
             oracle.attention(q, k, v, cq, ckv, w.num_heads, w.kv_num_heads, scale=w.scale or None,
-                             is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, threads=threads)
+                             is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, threads=threads,
+                             local_window=window)
             t_used += time.perf_counter() - t0
             el = 2 if w.dtype != "f32" else 4
             bytes_done += (q.numel() * 2 + k.numel() + v.numel()) * el
@@ -115,7 +118,7 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0):
                 "sample": f"{len(seqs)} of {len(batch.lq)} sequences, all {w.num_heads} heads "
                           f"({n_rows} rows), {t_used:.1f} s"}
     # prefill: random (token, head) rows of a few sequences, sized to the budget
-    keys = row_keys(batch.lq, batch.lkv, w.is_causal)
+    keys = row_keys(batch.lq, batch.lkv, w.is_causal, window)
     seqs = sorted(set(rng.choice(len(batch.lq), size=min(4, len(batch.lq)), replace=False).tolist()))
     q, k, v, cq, ckv, lq, lkv = sub_batch(batch, seqs)
     sub_keys = np.concatenate([keys[b] for b in seqs])
@@ -129,7 +132,7 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0):
         t0 = time.perf_counter()
         oracle.attention(q, k, v, cq, ckv, w.num_heads, w.kv_num_heads, scale=w.scale or None,
                          is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, rows=perm[:n_cal],
-                         threads=threads)
+                         threads=threads, local_window=window)
         t_cal = max(time.perf_counter() - t0, 1e-6)
         if t_cal >= 1.0 or n_cal >= n_all:
             break
@@ -143,7 +146,8 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0):
     t0 = time.perf_counter()
     for _ in range(reps):
         oracle.attention(q, k, v, cq, ckv, w.num_heads, w.kv_num_heads, scale=w.scale or None,
-                         is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, rows=perm[:n], threads=threads)
+                         is_causal=w.is_causal, softcap=w.softcap, dtype=w.dtype, rows=perm[:n], threads=threads,
+                         local_window=window)
     dt = (time.perf_counter() - t0) / reps
     return {"value": float(flops_per_row[:n].sum() / dt / 1e12), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
@@ -201,6 +205,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB mebibytes, 5 times (the known-size "
                          "reference that HBM byte counters are calibrated against), then exit")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="measure the workload with a local window of W keys per row (W > 0); FLOPs count "
+                         "only the pairs the window leaves visible")
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time a plain library bf16 GEMM (8192^3, torch.matmul -> hipBLASLt) on "
                          "zero, constant and N(0,1) operands, then exit: the MFMA rate the chip sustains "
@@ -243,18 +250,24 @@ def main(argv=None) -> int:
     cu_q = torch.from_numpy(batch.cu_q).cuda()
     cu_kv = torch.from_numpy(batch.cu_kv).cuda()
     out = torch.empty(batch.total_q, w.num_heads, w.dv, dtype=batch.q.dtype, device="cuda:0")
-    pairs = pva.valid_pairs(batch.cu_q, batch.cu_kv, w.is_causal)
+    window = a.window if a.window > 0 else 0
+    pairs = pva.valid_pairs(batch.cu_q, batch.cu_kv, w.is_causal, local_window=window or None)
     flops = 4.0 * pairs * w.num_heads * w.head_dim
     el = 4 if w.dtype == "f32" else 2
     io_bytes = (batch.q.numel() + batch.k.numel() + batch.v.numel() + out.numel()) * el
+    if window:
+        # K and V rows no query row of its sequence can see are never read
+        kv_rows = sum(b - max(0, b - a + 1 - window) if a else 0 for a, b in zip(batch.lq, batch.lkv))
+        io_bytes = (batch.q.numel() + out.numel()) * el + 2 * kv_rows * w.kv_num_heads * w.head_dim * el
     stats, _ = pva.plan(batch.cu_q, batch.cu_kv, w.num_heads, w.kv_num_heads, head_dim=w.head_dim,
-                        dtype=w.dtype, is_causal=w.is_causal, softcap=w.softcap)
+                        dtype=w.dtype, is_causal=w.is_causal, softcap=w.softcap, local_window=window or None)
     log(f"[bench] total_q={batch.total_q} total_kv={batch.total_kv} valid_pairs={pairs} plan={stats}")
 
     def step():
         pva.varlen_attn_fwd(batch.q, batch.k, batch.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads,
                             scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap, out=out,
-                            cu_seqlens_q_host=batch.cu_q, cu_seqlens_kv_host=batch.cu_kv)
+                            cu_seqlens_q_host=batch.cu_q, cu_seqlens_kv_host=batch.cu_kv,
+                            local_window=window or None)
 
     for _ in range(a.warmup):
         step()
@@ -291,7 +304,7 @@ def main(argv=None) -> int:
         achieved = flops / (avg / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS}
-    traffic = load_traffic(kind, a.workload) if kind in KERNEL_SOURCES else None
+    traffic = load_traffic(kind, a.workload) if kind in KERNEL_SOURCES and not window else None
     roof["traffic"] = traffic
     roof["kernel"] = kind
     roof["kernel_avg_ms"] = avg
@@ -300,14 +313,15 @@ def main(argv=None) -> int:
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(batch, decode, a.cpu_budget)
+        cpu = cpu_baseline(batch, decode, a.cpu_budget, window)
         log(f"[bench] cpu_baseline {cpu}")
 
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": a.workload, "batch": w.batch, "num_heads": w.num_heads,
+        "config": {"workload": a.workload + (f" + local window {window}" if window else ""),
+                   "local_window": window or None, "batch": w.batch, "num_heads": w.num_heads,
                    "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,
                    "softcap": w.softcap, "total_q": batch.total_q, "total_kv": batch.total_kv,
                    "valid_pairs": pairs, "flops_per_step": flops, "io_bytes_per_step": io_bytes,

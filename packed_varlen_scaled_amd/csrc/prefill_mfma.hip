@@ -269,7 +269,6 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       // max: it takes this tile's. Its O and l are still zero, so nothing
       // needs rescaling. Rows that see no key at all keep -inf.
       if (__builtin_expect(__any(m_ref == ninf()), 0)) {
-        asm volatile("" ::: "memory");
         float mx = ninf();
 #pragma unroll
         for (int mt = 0; mt < BN / 32; ++mt) {
@@ -380,16 +379,14 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
         if (!skips(kt)) compute(t & 1, kt, std::integral_constant<int, kSafe>{});
       }
     } else {
-      // regions: first tile | masked (left window edge) | plain | masked
+      // regions: first tile | plain | masked. A window whose left edge
+      // reaches past tile 1 for some row (only items of 128 rows) gets no
+      // plain region: a third loop instantiation of the tile body makes the
+      // compiler move the accumulators to scratch memory.
       if (n_tiles > 0) compute(0, step(0), std::integral_constant<int, kFirst>{});
-      const int p0 = min(t_plain0, n_tiles);
-      const int p1 = max(p0, min(t_plain1, n_tiles));
-      for (int t = 1; t < p0; ++t) {
-        const int kt = step(t);
-        if (!skips(kt)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
-      }
-      for (int t = p0; t < p1; ++t) compute(t & 1, step(t), std::integral_constant<int, kPlain>{});
-      for (int t = max(p1, 1); t < n_tiles; ++t) {
+      const int p1 = t_plain0 > 1 ? 1 : max(1, min(t_plain1, n_tiles));
+      for (int t = 1; t < p1; ++t) compute(t & 1, step(t), std::integral_constant<int, kPlain>{});
+      for (int t = p1; t < n_tiles; ++t) {
         const int kt = step(t);
         if (!skips(kt)) compute(t & 1, kt, std::integral_constant<int, kMasked>{});
       }

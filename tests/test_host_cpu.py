@@ -282,3 +282,19 @@ def test_workload_plans_fit():
         assert stats["workspace_bytes"] < 512 << 20
         if name == "packed_decode":
             assert stats["n_decode_items"] >= 1024
+
+
+def test_kernels_keep_their_working_set_in_registers():
+    """No kernel of the last build uses scratch memory or spills registers (the
+    compiler's own kernel-resource report, recorded by the build): a private
+    array demoted to scratch in a tile loop costs an order of magnitude."""
+    import json
+    from packed_varlen_scaled_amd import build as b
+    with open(b.RESOURCES_PATH) as f:
+        recs = json.load(f)
+    kernels = [r for r in recs if r["kernel"].startswith("_ZN3pva")]
+    assert len(kernels) >= 20, kernels
+    for r in kernels:
+        assert r.get("scratch_bytes_per_lane", 0) == 0, r
+        assert r.get("vgpr_spill", 0) == 0, r
+        assert r.get("waves_per_simd", 0) >= 1, r
