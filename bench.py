@@ -208,6 +208,10 @@ def main(argv=None) -> int:
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="measure the workload with a local window of W keys per row (W > 0); FLOPs count "
                          "only the pairs the window leaves visible")
+    ap.add_argument("--path", choices=["host", "device", "graph"], default="host",
+                    help="host: varlen_attn_fwd (host scheduler, host cu mirrors); device: "
+                         "varlen_attn_fwd_device (device scheduler, no host work per call); graph: one "
+                         "device-path call captured in a HIP graph, the timed steps are replays")
     ap.add_argument("--gemm-ceiling", action="store_true",
                     help="only time a plain library bf16 GEMM (8192^3, torch.matmul -> hipBLASLt) on "
                          "zero, constant and N(0,1) operands, then exit: the MFMA rate the chip sustains "
@@ -263,28 +267,74 @@ def main(argv=None) -> int:
                         dtype=w.dtype, is_causal=w.is_causal, softcap=w.softcap, local_window=window or None)
     log(f"[bench] total_q={batch.total_q} total_kv={batch.total_kv} valid_pairs={pairs} plan={stats}")
 
-    def step():
+    def step_host():
         pva.varlen_attn_fwd(batch.q, batch.k, batch.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads,
                             scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap, out=out,
                             cu_seqlens_q_host=batch.cu_q, cu_seqlens_kv_host=batch.cu_kv,
                             local_window=window or None)
 
+    ws = latch = None
+    if a.path != "host":
+        ws = torch.empty(pva.device_workspace_bytes(len(batch.lq), batch.total_q, batch.total_kv, w.num_heads,
+                                                    w.kv_num_heads, w.head_dim, w.dv, w.dtype),
+                         dtype=torch.uint8, device="cuda:0")
+        latch = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+
+    def step_device():
+        pva.varlen_attn_fwd_device(batch.q, batch.k, batch.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads,
+                                   scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap,
+                                   local_window=window or None, out=out, workspace=ws, error_latch=latch)
+
+    step = step_host if a.path == "host" else step_device
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps")
-    pva.profile_enable(True)
+    graph = None
+    if a.path == "graph":
+        # kernel times come from eagerly launched device-path steps (a graph
+        # replay records no events); the timed steps below are replays
+        pva.profile_enable(True)
+        for _ in range(a.steps):
+            step()
+        torch.cuda.synchronize()
+        prof_graph = pva.profile_read()
+        pva.profile_enable(False)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(a.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps ({a.path} path)")
+    if graph is None:
+        pva.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     host_s = 0.0
     for _ in range(a.steps):
         h0 = time.perf_counter()
-        step()
+        if graph is None:
+            step()
+        else:
+            graph.replay()
         host_s += time.perf_counter() - h0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    prof = pva.profile_read()
-    pva.profile_enable(False)
+    if graph is None:
+        prof = pva.profile_read()
+        pva.profile_enable(False)
+    else:
+        prof = prof_graph
+    if latch is not None and int(latch.item()) != 0:
+        log(f"[bench] error latch set: {int(latch.item())}")
+        return 1
     ms = elapsed / a.steps * 1e3
     log(f"[bench] {ms:.4f} ms/step; host call {host_s / a.steps * 1e3:.4f} ms/step; kernels {prof}")
 
@@ -321,7 +371,7 @@ def main(argv=None) -> int:
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": a.workload + (f" + local window {window}" if window else ""),
-                   "local_window": window or None, "batch": w.batch, "num_heads": w.num_heads,
+                   "local_window": window or None, "call": a.path, "batch": w.batch, "num_heads": w.num_heads,
                    "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,
                    "softcap": w.softcap, "total_q": batch.total_q, "total_kv": batch.total_kv,
                    "valid_pairs": pairs, "flops_per_step": flops, "io_bytes_per_step": io_bytes,

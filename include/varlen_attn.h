@@ -168,6 +168,59 @@ varlen_status_t varlen_attn_fwd_ex(const void* q, const void* k, const void* v,
                                    const varlen_attn_options_t* options);
 
 /*
+ * varlen_attn_fwd_device -- the same op for callers that cannot wait for the
+ * host: CUDA/HIP-graph capture and replay, or loops that must never stall on
+ * a device-to-host read. The packed op of the pages reads cu_seqlens back and
+ * synchronises, so it cannot be captured (page
+ * src/kernels/packed_varlen_attention.rs, capture_support); this entry point
+ * builds the work list on the device instead, validates the cu arrays there
+ * and reports violations through an error latch, as the GQA op's capture-safe
+ * decode does (page src/kernels/group_query_attention.rs,
+ * gqa_prepare_metadata and its capture-error bit flags).
+ *
+ * The call enqueues a scheduler kernel and the attention kernels on `stream`
+ * and returns. It reads no host memory, allocates nothing, copies nothing
+ * from the host and never synchronises, so it can be captured into a graph;
+ * a replay reads the cu arrays (and q, k, v) as they are at replay time.
+ *
+ *  q, k, v, out   as varlen_attn_fwd
+ *  cu_seqlens_q, cu_seqlens_kv
+ *                 device int32 [batch + 1], read only on the device
+ *  total_q        rows of the q and out buffers; cu_seqlens_q[batch] may be
+ *                 any value up to it (rows past it are not written)
+ *  total_kv       rows of the k and v buffers; cu_seqlens_kv[batch] <= it
+ *  local_window   as the options field of varlen_attn_fwd_ex (-1 or 0: none)
+ *  workspace      device memory of at least
+ *                 varlen_attn_device_workspace_bytes(...) bytes, 256-byte
+ *                 aligned, owned by the caller; a call overwrites it, so
+ *                 calls that overlap on the device need separate workspaces
+ *  error_latch    device int32, owned by the caller, zero before first use.
+ *                 The scheduler ORs a violation into it: 1 cu_seqlens_q[0]
+ *                 != 0, 2 cu_seqlens_q decreases, 4 cu_seqlens_q[batch] >
+ *                 total_q, 8/16/32 the same for cu_seqlens_kv, 64 internal
+ *                 list overflow. While it is non-zero, calls compute nothing
+ *                 and leave out untouched; clear it (with a kernel, not a
+ *                 memset, inside a graph) to resume.
+ *
+ * Host-side argument errors return their status before anything is enqueued
+ * (the rules of varlen_attn_fwd, on the scalars only). The same GPU kernels
+ * as varlen_attn_fwd run on the same items, so the results are bitwise those
+ * of varlen_attn_fwd with default options.
+ */
+size_t varlen_attn_device_workspace_bytes(int32_t batch, int64_t total_q, int64_t total_kv,
+                                          int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                          int32_t v_head_dim, int32_t dtype);
+
+varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void* v,
+                                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                       int32_t batch, int64_t total_q, int64_t total_kv,
+                                       int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                       int32_t v_head_dim, int32_t dtype, float scale,
+                                       int32_t is_causal, float softcap, int32_t local_window,
+                                       void* out, void* workspace, size_t workspace_bytes,
+                                       int32_t* error_latch, void* stream);
+
+/*
  * varlen_attn_plan -- the host-side work scheduler on its own (no device
  * work, no HIP call; usable without a GPU). It validates like
  * varlen_attn_fwd (with host cu arrays) and fills `stats` with what a call
@@ -235,10 +288,11 @@ int64_t varlen_attn_valid_pairs_window(const int32_t* cu_seqlens_q_host,
  * kernel it launches. varlen_attn_profile_read waits for the recorded events,
  * adds their elapsed times to per-kernel totals and returns the totals since
  * the last enable. Index k of the arrays: 0 prefill (MFMA), 1 prefill
- * (fp32), 2 split-KV decode, 3 combine, 4 work-list upload.
+ * (fp32), 2 split-KV decode, 3 combine, 4 work-list upload, 5 device
+ * scheduler (varlen_attn_fwd_device).
  * varlen_attn_profile_enable(0) stops recording; (1) clears and starts.
  */
-#define VARLEN_PROFILE_KINDS 5
+#define VARLEN_PROFILE_KINDS 6
 typedef struct {
   double total_ms[VARLEN_PROFILE_KINDS];
   int64_t launches[VARLEN_PROFILE_KINDS];

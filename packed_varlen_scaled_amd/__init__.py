@@ -59,11 +59,16 @@ class PlanStats(ctypes.Structure):
 
 
 class ProfileTotals(ctypes.Structure):
-    _fields_ = [("total_ms", ctypes.c_double * 5), ("launches", ctypes.c_int64 * 5),
-                ("items", ctypes.c_int64 * 5)]
+    _fields_ = [("total_ms", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6),
+                ("items", ctypes.c_int64 * 6)]
 
 
-PROFILE_KINDS = ("prefill_mfma", "prefill_f32", "decode", "combine", "upload")
+PROFILE_KINDS = ("prefill_mfma", "prefill_f32", "decode", "combine", "upload", "device_plan")
+
+# Bits of the device path's error latch (include/varlen_attn.h, varlen_attn_fwd_device).
+LATCH_BITS = {1: "cu_seqlens_q[0] != 0", 2: "cu_seqlens_q decreases", 4: "cu_seqlens_q[batch] > total_q",
+              8: "cu_seqlens_kv[0] != 0", 16: "cu_seqlens_kv decreases", 32: "cu_seqlens_kv[batch] > total_kv",
+              64: "work list overflow"}
 
 
 def library_path() -> str:
@@ -84,6 +89,11 @@ def load_library():
     lib.varlen_attn_fwd.restype = ctypes.c_int
     lib.varlen_attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Options)]
     lib.varlen_attn_fwd_ex.restype = ctypes.c_int
+    lib.varlen_attn_device_workspace_bytes.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32]
+    lib.varlen_attn_device_workspace_bytes.restype = ctypes.c_size_t
+    lib.varlen_attn_fwd_device.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, i32, f32,
+                                           i32, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.varlen_attn_fwd_device.restype = ctypes.c_int
     lib.varlen_attn_plan.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, i32, f32,
                                      ctypes.POINTER(Options), ctypes.POINTER(PlanStats), vp, i64]
     lib.varlen_attn_plan.restype = ctypes.c_int
@@ -214,6 +224,66 @@ def varlen_attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num
             n - 1, tq, tkv, hq, hkv, d, dv, code,
             float(scale) if scale else 0.0, 1 if is_causal else 0, float(softcap),
             out.data_ptr(), stream, ctypes.byref(opts))
+    _check(st)
+    return out
+
+
+def device_workspace_bytes(batch: int, total_q: int, total_kv: int, num_heads: int, kv_num_heads=None,
+                           head_dim: int = 128, v_head_dim: int = 0, dtype: str = "bf16") -> int:
+    """Bytes of workspace varlen_attn_fwd_device needs for these buffer sizes."""
+    n = load_library().varlen_attn_device_workspace_bytes(int(batch), int(total_q), int(total_kv), int(num_heads),
+                                                          int(kv_num_heads or 0), int(head_dim), int(v_head_dim),
+                                                          DTYPE_CODES[dtype])
+    if n == 0:
+        raise ValueError("invalid sizes for the device workspace")
+    return int(n)
+
+
+def varlen_attn_fwd_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None,
+                           scale=None, is_causal: bool = False, softcap: float = 0.0, local_window=None,
+                           out=None, workspace=None, error_latch=None, stream=None):
+    """The capture-safe call: cu_seqlens are read only on the device, nothing is
+    allocated, copied from the host or waited for. ``workspace`` is a CUDA(HIP)
+    uint8 tensor of at least ``device_workspace_bytes(...)`` bytes and
+    ``error_latch`` an int32 CUDA tensor of one element, zero before first use
+    (see LATCH_BITS). The rows of q/out and k/v are the buffer capacities;
+    cu_seqlens_*[-1] may be smaller. Returns ``out``."""
+    import torch
+    lib = load_library()
+    hq = int(num_heads)
+    hkv = int(kv_num_heads) if kv_num_heads else hq
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("Q, K, and V must use the same floating dtype")
+    tq, d = _resolve(q, hq, "query")
+    tkv, dk = _resolve(k, hkv, "key")
+    tv, dv = _resolve(v, hkv, "value")
+    if dk != d or tv != tkv:
+        raise ValueError("key head size / token count must match query head size / value token count")
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    if out.dtype != q.dtype or not out.is_contiguous() or out.numel() != tq * hq * dv or not out.is_cuda:
+        raise ValueError("output must be a contiguous GPU tensor of the Q/K/V dtype with [total_q, num_heads, v_head_size] elements")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if cu is None or not cu.is_cuda or cu.dtype != torch.int32 or not cu.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_kv.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv lengths differ")
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if error_latch is None or not error_latch.is_cuda or error_latch.dtype != torch.int32:
+        raise ValueError("error_latch must be an int32 GPU tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib.varlen_attn_fwd_device(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr(),
+            cu_seqlens_q.numel() - 1, tq, tkv, hq, hkv, d, dv, code,
+            float(scale) if scale else 0.0, 1 if is_causal else 0, float(softcap),
+            -1 if local_window is None else int(local_window), out.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), error_latch.data_ptr(), stream)
     _check(st)
     return out
 

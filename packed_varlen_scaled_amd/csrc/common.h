@@ -49,7 +49,44 @@ __host__ __device__ inline int64_t partial_index(const WorkItem& it, int split, 
   return (int64_t)it.partial_base + ((int64_t)split * it.q_rows + row) * it.heads + hh;
 }
 
+// Device-built work list (the device scheduler, sched.hip): where it writes
+// the lists, the per-sequence list offsets, the item counts, and the bounds
+// the launch grids were sized for.
+enum DeviceHeader : int32_t {
+  kHdrPrefill = 0,   // items in the prefill list
+  kHdrDecode = 1,    // items in the split-KV decode list
+  kHdrCombine = 2,   // items in the combine list
+  kHdrPartials = 3,  // partial rows used
+  kHdrChunk = 4,     // split-KV chunk (keys)
+  kHdrInts = 64,     // header size in int32 (256 bytes)
+};
+// Bits of the caller's error latch.
+enum LatchBits : int32_t {
+  kLatchCuQStart = 1,     // cu_seqlens_q[0] != 0
+  kLatchCuQOrder = 2,     // cu_seqlens_q decreases
+  kLatchCuQTotal = 4,     // cu_seqlens_q[B] > the query buffer's rows
+  kLatchCuKvStart = 8,    // cu_seqlens_kv[0] != 0
+  kLatchCuKvOrder = 16,   // cu_seqlens_kv decreases
+  kLatchCuKvTotal = 32,   // cu_seqlens_kv[B] > the key/value buffers' rows
+  kLatchCapacity = 64,    // a list outgrew its bound (not expected)
+};
+struct DevicePlan {
+  int32_t batch, hq;
+  int32_t nh, rows_per_item, prefill_kind;  // prefill items: nh heads x rows_per_item rows
+  int32_t nh_dec, use_decode;               // decode items: nh_dec heads, L_q == 1 sequences
+  int32_t causal, window;
+  int32_t cap_q, cap_kv;                    // rows of the q/out and k/v buffers
+  int64_t cap_prefill, cap_decode, cap_combine, cap_partials;
+  int32_t* header;
+  // [batch + 1] each, used when the batch is too large for the scheduler's LDS
+  int32_t *seq_q, *seq_kv, *seq_pre, *seq_decf, *seq_decp, *seq_cmb, *seq_part;
+  WorkItem *prefill, *decode, *combine;
+};
+
 struct Params {
+  // Items of the launch: with a device-built list the grid is an upper bound
+  // and workgroups at or past *item_count return at once; null otherwise.
+  const int32_t* item_count;
   const void* q;
   const void* k;
   const void* v;

@@ -46,6 +46,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
   __shared__ float red_m[NW][16];
   __shared__ float red_l[NW][16];
 
+  if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
 // n_splits partials in split order.
 template <int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(Params p, const WorkItem* __restrict__ items) {
+  if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
   const WorkItem it = items[blockIdx.x];
   const int dv = p.dv;
   const int total = it.q_rows * it.heads * dv;

@@ -21,6 +21,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(Params p, const WorkIt
   __shared__ float vs[BN][MAXD + 1];
   __shared__ float ps[BM][BN + 1];
 
+  if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
   const int row = tid >> 3;  // tile row owned by this group of 8 lanes

@@ -79,6 +79,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   // c ^ chunk_perm<D>(r).
   __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];
 
+  if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;
   const int lane = tid & 63;

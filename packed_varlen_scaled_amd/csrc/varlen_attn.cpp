@@ -27,6 +27,8 @@ hipError_t launch_prefill_mfma(const Params& p, const WorkItem* items, int n, in
 hipError_t launch_decode(const Params& p, const WorkItem* items, int n, int dtype, hipStream_t s);
 hipError_t launch_combine(const Params& p, const WorkItem* items, int n, int dtype, hipStream_t s);
 hipError_t launch_prefill_f32(const Params& p, const WorkItem* items, int n, hipStream_t s);
+hipError_t launch_plan(const DevicePlan& dp, const int32_t* cu_q, const int32_t* cu_kv, int32_t* latch,
+                       hipStream_t s);
 }  // namespace pva
 
 namespace {
@@ -386,6 +388,63 @@ Layout layout_of(const Plan& plan, int32_t dv) {
 }
 
 // ---------------------------------------------------------------------------
+// Device-built work list: item shapes (the host scheduler's), list bounds
+// that size the launch grids, and the caller's workspace layout.
+// ---------------------------------------------------------------------------
+struct DeviceShape {
+  int nh = 1, rows_per_item = 32, prefill_kind = pva::kPrefillMfma, waves = 4;
+  int nh_dec = 1, use_decode = 0;
+  int64_t cap_prefill = 0, cap_decode = 0, cap_combine = 0, cap_partials = 0;
+  size_t hdr_off = 0, seq_off = 0, pre_off = 0, dec_off = 0, cmb_off = 0, lse_off = 0, po_off = 0, total = 0;
+};
+
+DeviceShape device_shape(const Problem& pr) {
+  DeviceShape d;
+  const int64_t B = pr.batch;
+  if (pr.dtype == VARLEN_F32) {
+    d.nh = 1;
+    d.rows_per_item = 32;
+    d.prefill_kind = pva::kPrefillF32;
+    d.waves = 4;
+    d.use_decode = 0;
+  } else {
+    d.nh = largest_pow2_divisor_upto(pr.group, 8);
+    const int rblocks = d.nh >= 4 ? 1 : 4 / d.nh;
+    d.rows_per_item = 32 * rblocks;
+    d.waves = d.nh * rblocks;
+    d.nh_dec = largest_pow2_divisor_upto(pr.group, 16);
+    d.use_decode = 1;
+  }
+  // every sequence adds at most one partial row block
+  d.cap_prefill = ((pr.total_q + d.rows_per_item - 1) / d.rows_per_item + B) * (pr.hq / d.nh);
+  if (d.use_decode) {
+    // The split-KV chunk is at least ceil(decode keys * groups / 2048) unless
+    // clamped to 8192, so a group splits into at most
+    // max(2048 / groups, total_kv / 8192) + 1 + B items.
+    const int64_t g = pr.hq / d.nh_dec;
+    const int64_t per = std::max<int64_t>((2048 + g - 1) / g, (pr.total_kv + 8191) / 8192) + 1 + B;
+    d.cap_decode = g * per;
+    d.cap_combine = g * B;
+    d.cap_partials = d.cap_decode * d.nh_dec;
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  d.hdr_off = take(sizeof(int32_t) * pva::kHdrInts);
+  d.seq_off = take(sizeof(int32_t) * 7 * (size_t)(B + 1));
+  d.pre_off = take(sizeof(WorkItem) * (size_t)d.cap_prefill);
+  d.dec_off = take(sizeof(WorkItem) * (size_t)d.cap_decode);
+  d.cmb_off = take(sizeof(WorkItem) * (size_t)d.cap_combine);
+  d.lse_off = take(sizeof(float) * (size_t)d.cap_partials);
+  d.po_off = take(sizeof(float) * (size_t)d.cap_partials * (size_t)pr.dv);
+  d.total = off;
+  return d;
+}
+
+// ---------------------------------------------------------------------------
 // Per-device workspace.
 // ---------------------------------------------------------------------------
 struct DeviceState {
@@ -616,6 +675,123 @@ varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* 
   return VARLEN_OK;
 }
 
+// The capture-safe call: no host copy of the cu arrays, no synchronisation,
+// no allocation, no host-to-device copy. The work list is built on the device
+// into the caller's workspace; total_q / total_kv are the rows of the q/out
+// and k/v buffers.
+varlen_status_t run_device(const void* q, const void* k, const void* v, const int32_t* cu_q_dev,
+                           const int32_t* cu_kv_dev, int32_t batch, int64_t total_q, int64_t total_kv,
+                           int32_t num_heads, int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                           int32_t dtype, float scale, int32_t is_causal, float softcap, int32_t local_window,
+                           void* out, void* workspace, size_t workspace_bytes, int32_t* latch, void* stream_v) {
+  g_last_error.clear();
+  Problem pr;
+  varlen_status_t st = check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim,
+                                     dtype, scale, softcap, &pr);
+  if (st != VARLEN_OK) return st;
+  pr.causal = is_causal != 0;
+  if ((st = check_window(local_window, &pr)) != VARLEN_OK) return st;
+  if ((st = check_supported(pr)) != VARLEN_OK) return st;
+  if (!cu_q_dev || !cu_kv_dev || !latch)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "device cu_seqlens arrays and the error latch must be non-null");
+  if (total_q > 0 && (!q || !out))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "query and output pointers must be non-null");
+  if (total_kv > 0 && (!k || !v))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "key and value pointers must be non-null");
+  const DeviceShape sh = device_shape(pr);
+  if (!workspace || workspace_bytes < sh.total)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "workspace holds %zu bytes, the call needs %zu (varlen_attn_device_workspace_bytes)",
+                workspace ? workspace_bytes : (size_t)0, sh.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (sh.cap_prefill > INT32_MAX || sh.cap_decode > INT32_MAX || sh.cap_partials > INT32_MAX)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "the batch is too large for one launch");
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  char* ws = static_cast<char*>(workspace);
+
+  pva::DevicePlan dp;
+  std::memset(&dp, 0, sizeof dp);
+  dp.batch = pr.batch;
+  dp.hq = pr.hq;
+  dp.nh = sh.nh;
+  dp.rows_per_item = sh.rows_per_item;
+  dp.prefill_kind = sh.prefill_kind;
+  dp.nh_dec = sh.nh_dec;
+  dp.use_decode = sh.use_decode;
+  dp.causal = pr.causal;
+  dp.window = pr.window;
+  dp.cap_q = (int32_t)total_q;
+  dp.cap_kv = (int32_t)total_kv;
+  dp.cap_prefill = sh.cap_prefill;
+  dp.cap_decode = sh.cap_decode;
+  dp.cap_combine = sh.cap_combine;
+  dp.cap_partials = sh.cap_partials;
+  dp.header = reinterpret_cast<int32_t*>(ws + sh.hdr_off);
+  int32_t* seq = reinterpret_cast<int32_t*>(ws + sh.seq_off);
+  const int64_t nb = (int64_t)pr.batch + 1;
+  dp.seq_q = seq;
+  dp.seq_kv = seq + nb;
+  dp.seq_pre = seq + 2 * nb;
+  dp.seq_decf = seq + 3 * nb;
+  dp.seq_decp = seq + 4 * nb;
+  dp.seq_cmb = seq + 5 * nb;
+  dp.seq_part = seq + 6 * nb;
+  dp.prefill = reinterpret_cast<WorkItem*>(ws + sh.pre_off);
+  dp.decode = reinterpret_cast<WorkItem*>(ws + sh.dec_off);
+  dp.combine = reinterpret_cast<WorkItem*>(ws + sh.cmb_off);
+
+  pva::Params p;
+  std::memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.part_lse = reinterpret_cast<float*>(ws + sh.lse_off);
+  p.part_o = reinterpret_cast<float*>(ws + sh.po_off);
+  p.hq = pr.hq;
+  p.hkv = pr.hkv;
+  p.group = pr.group;
+  p.d = pr.d;
+  p.dv = pr.dv;
+  p.causal = pr.causal;
+  p.window = pr.window;
+  p.softcap_on = pr.softcap != 0.f;
+  const float log2e = 1.4426950408889634f;
+  p.scale = pr.scale;
+  p.softcap = pr.softcap;
+  p.score_log2 = pr.scale * log2e;
+  if (p.softcap_on) {
+    p.cap_log2 = pr.softcap * log2e;
+    p.tanh_log2 = 2.f * pr.scale / pr.softcap * log2e;
+  }
+
+  hipError_t e = timed(5, 1, stream, [&] { return pva::launch_plan(dp, cu_q_dev, cu_kv_dev, latch, stream); });
+  pva::Params pp = p;
+  if (e == hipSuccess && sh.cap_prefill > 0) {
+    pp.item_count = dp.header + pva::kHdrPrefill;
+    if (pr.dtype == VARLEN_F32) {
+      e = timed(1, sh.cap_prefill, stream,
+                [&] { return pva::launch_prefill_f32(pp, dp.prefill, (int)sh.cap_prefill, stream); });
+    } else {
+      e = timed(0, sh.cap_prefill, stream, [&] {
+        return pva::launch_prefill_mfma(pp, dp.prefill, (int)sh.cap_prefill, pr.dtype, sh.waves, stream);
+      });
+    }
+  }
+  if (e == hipSuccess && sh.cap_decode > 0) {
+    pp.item_count = dp.header + pva::kHdrDecode;
+    e = timed(2, sh.cap_decode, stream,
+              [&] { return pva::launch_decode(pp, dp.decode, (int)sh.cap_decode, pr.dtype, stream); });
+  }
+  if (e == hipSuccess && sh.cap_combine > 0) {
+    pp.item_count = dp.header + pva::kHdrCombine;
+    e = timed(3, sh.cap_combine, stream,
+              [&] { return pva::launch_combine(pp, dp.combine, (int)sh.cap_combine, pr.dtype, stream); });
+  }
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return VARLEN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -629,6 +805,31 @@ varlen_status_t varlen_attn_fwd(const void* q, const void* k, const void* v, con
   return run(q, k, v, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_q_host, cu_seqlens_kv_host, batch, total_q,
              total_kv, num_heads, kv_num_heads, head_dim, v_head_dim, dtype, scale, is_causal, softcap, out, stream,
              nullptr);
+}
+
+size_t varlen_attn_device_workspace_bytes(int32_t batch, int64_t total_q, int64_t total_kv, int32_t num_heads,
+                                          int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                                          int32_t dtype) {
+  g_last_error.clear();
+  Problem pr;
+  if (check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim, dtype, 0.f, 0.f,
+                    &pr) != VARLEN_OK)
+    return 0;
+  pr.causal = 0;
+  pr.window = 0;
+  return device_shape(pr).total;
+}
+
+varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_kv, int32_t batch, int64_t total_q,
+                                       int64_t total_kv, int32_t num_heads, int32_t kv_num_heads,
+                                       int32_t head_dim, int32_t v_head_dim, int32_t dtype, float scale,
+                                       int32_t is_causal, float softcap, int32_t local_window, void* out,
+                                       void* workspace, size_t workspace_bytes, int32_t* error_latch,
+                                       void* stream) {
+  return run_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv, num_heads, kv_num_heads,
+                    head_dim, v_head_dim, dtype, scale, is_causal, softcap, local_window, out, workspace,
+                    workspace_bytes, error_latch, stream);
 }
 
 varlen_status_t varlen_attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,

@@ -323,3 +323,166 @@ def test_local_window_full_size_sampled():
     assert torch.isfinite(out.float()).all()
     del batch, out
     torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------
+# Device-scheduled, capture-safe calls (varlen_attn_fwd_device).
+# --------------------------------------------------------------------------
+def _device_call(batch, out, ws, latch, local_window=None, cu_q=None, cu_kv=None):
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = batch.workload
+    cu_q = torch.from_numpy(batch.cu_q).cuda() if cu_q is None else cu_q
+    cu_kv = torch.from_numpy(batch.cu_kv).cuda() if cu_kv is None else cu_kv
+    return pva.varlen_attn_fwd_device(batch.q, batch.k, batch.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads,
+                                      scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap,
+                                      local_window=local_window, out=out, workspace=ws, error_latch=latch)
+
+
+def _device_buffers(batch):
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = batch.workload
+    n = pva.device_workspace_bytes(len(batch.lq), batch.total_q, batch.total_kv, w.num_heads, w.kv_num_heads,
+                                   w.head_dim, w.dv, w.dtype)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    latch = torch.zeros(1, dtype=torch.int32, device="cuda")
+    return ws, latch
+
+
+DEVICE = [
+    ("bf16_gqa4_causal", dict(hq=8, hkv=2), [70, 1, 129, 33, 0, 200], [70, 1, 129, 33, 5, 200], None),
+    ("bf16_decode_mix_softcap", dict(hq=16, hkv=2, softcap=20.0), [1, 100, 1, 257, 1], [3000, 700, 129, 300, 5], None),
+    ("bf16_window", dict(hq=8, hkv=2), [40, 3, 100, 1], [300, 90, 100, 1700], 64),
+    ("bf16_mha_rows4", dict(hq=2, hkv=2, causal=False), [300, 77], [300, 900], None),
+    ("f16_gqa8", dict(dtype="f16", hq=16, hkv=2), [150, 64, 1], [150, 64, 900], None),
+    ("bf16_d64", dict(hq=8, hkv=2, d=64), [100, 1, 37], [100, 513, 37], None),
+    ("f32_gqa", dict(dtype="f32", hq=8, hkv=2, d=64), [70, 1, 33], [70, 200, 40], None),
+]
+
+
+@pytest.mark.parametrize("name,kw,lq,lkv,window", DEVICE, ids=[c[0] for c in DEVICE])
+def test_device_scheduled_call_equals_host_planned_call(name, kw, lq, lkv, window):
+    """The device scheduler emits the host scheduler's items, so the same
+    kernels give the same bits."""
+    import torch
+    w = _workload(**kw)
+    _say("device", name, lq, lkv, window)
+    batch = _batch(w, lq, lkv)
+    want = run_gpu(batch, local_window=window).clone()
+    ws, latch = _device_buffers(batch)
+    out = torch.full_like(want, 7.0)
+    _device_call(batch, out, ws, latch, local_window=window)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0
+    assert torch.equal(out, want)
+    # and against the oracle
+    compare(out.double().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv),
+            oracle_all(batch, local_window=window or 0), w.dtype)
+
+
+def test_device_scheduler_latches_bad_cu_seqlens():
+    import torch
+    w = _workload(hq=8, hkv=2)
+    batch = _batch(w, [40, 30], [40, 30])
+    ws, latch = _device_buffers(batch)
+    sentinel = torch.full((batch.total_q, 8, 128), 3.0, dtype=batch.q.dtype, device="cuda")
+    cases = [([1, 40, 70], [0, 40, 70], 1), ([0, 40, 30], [0, 40, 70], 2), ([0, 40, 71], [0, 40, 70], 4),
+             ([0, 40, 70], [2, 40, 70], 8), ([0, 40, 70], [0, 50, 45], 16), ([0, 40, 70], [0, 40, 80], 32)]
+    for cq, ckv, bit in cases:
+        _say("latch", cq, ckv, bit)
+        latch.zero_()
+        out = sentinel.clone()
+        _device_call(batch, out, ws, latch, cu_q=torch.tensor(cq, dtype=torch.int32, device="cuda"),
+                     cu_kv=torch.tensor(ckv, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        assert int(latch.item()) == bit
+        assert torch.equal(out, sentinel)
+    # latch first: a valid call while the latch is set computes nothing
+    out = sentinel.clone()
+    _device_call(batch, out, ws, latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 32 and torch.equal(out, sentinel)
+    latch.zero_()
+    _device_call(batch, out, ws, latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0 and torch.equal(out, run_gpu(batch))
+
+
+def test_graph_capture_replays_with_new_lengths():
+    """Capture one call into a HIP graph, then replay it with new cu_seqlens
+    (fewer or more rows inside the same buffers) and new data: every replay
+    equals the eager host-planned call on the same inputs, bit for bit."""
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = _workload(hq=16, hkv=2, softcap=20.0)
+    cap_q, cap_kv, B = 700, 6000, 5
+    big = _batch(w, [100, 1, 257, 1, 340], [700, 3000, 300, 1500, 500])
+    assert big.total_q <= cap_q and big.total_kv <= cap_kv
+    q = torch.zeros(cap_q, 16, 128, dtype=big.q.dtype, device="cuda")
+    k = torch.zeros(cap_kv, 2, 128, dtype=big.q.dtype, device="cuda")
+    v = torch.zeros(cap_kv, 2, 128, dtype=big.q.dtype, device="cuda")
+    out = torch.zeros(cap_q, 16, 128, dtype=big.q.dtype, device="cuda")
+    cu_q = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    cu_kv = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    n = pva.device_workspace_bytes(B, cap_q, cap_kv, 16, 2, 128)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    latch = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def load(bt):
+        q.zero_(), k.zero_(), v.zero_()
+        q[:bt.total_q].copy_(bt.q)
+        k[:bt.total_kv].copy_(bt.k)
+        v[:bt.total_kv].copy_(bt.v)
+        cu_q.copy_(torch.from_numpy(bt.cu_q))
+        cu_kv.copy_(torch.from_numpy(bt.cu_kv))
+
+    def call():
+        pva.varlen_attn_fwd_device(q, k, v, cu_q, cu_kv, 16, 2, is_causal=True, softcap=20.0, out=out,
+                                   workspace=ws, error_latch=latch)
+
+    load(big)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    _say("capturing")
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    shapes = [([100, 1, 257, 1, 340], [700, 3000, 300, 1500, 500]), ([5, 60, 1, 1, 200], [5, 4000, 800, 1, 900]),
+              ([300, 1, 0, 200, 150], [300, 2, 0, 700, 2000]), ([1, 1, 1, 1, 1], [5000, 100, 1, 1, 300])]
+    for rep, (lq, lkv) in enumerate(shapes):
+        bt = _batch(_workload(hq=16, hkv=2, softcap=20.0, seed=40 + rep), lq, lkv)
+        want = run_gpu(bt).clone()  # eager host-planned call
+        load(bt)
+        out.fill_(5.0)
+        torch.cuda.synchronize()
+        _say("replay", rep, lq, lkv)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(latch.item()) == 0
+        assert torch.equal(out[:bt.total_q], want), rep
+        assert bool((out[bt.total_q:] == 5.0).all()), rep  # rows past cu_seqlens_q[-1] untouched
+
+
+def test_device_scheduler_large_batch():
+    """3000 short sequences (prefill and decode mixed): the scheduler keeps its
+    per-sequence offsets in the workspace instead of LDS."""
+    import torch
+    w = _workload(hq=8, hkv=2, softcap=10.0)
+    rng = np.random.default_rng(9)
+    lq = [int(x) if x > 1 else 1 for x in rng.integers(0, 12, size=3000)]
+    lkv = [a + int(p) for a, p in zip(lq, rng.integers(0, 40, size=3000))]
+    _say("device large batch", len(lq), sum(lq), sum(lkv))
+    batch = _batch(w, lq, lkv)
+    want = run_gpu(batch).clone()
+    ws, latch = _device_buffers(batch)
+    out = torch.full_like(want, 7.0)
+    _device_call(batch, out, ws, latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0
+    assert torch.equal(out, want)

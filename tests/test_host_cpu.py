@@ -298,3 +298,44 @@ def test_kernels_keep_their_working_set_in_registers():
         assert r.get("scratch_bytes_per_lane", 0) == 0, r
         assert r.get("vgpr_spill", 0) == 0, r
         assert r.get("waves_per_simd", 0) >= 1, r
+
+
+# --------------------------------------------------------------------------
+# The device-scheduled (capture-safe) entry point: host-side checks only.
+# --------------------------------------------------------------------------
+def test_device_workspace_size():
+    small = pva.device_workspace_bytes(4, 1000, 1000, 32, 8)
+    assert small > 0 and small % 256 == 0
+    assert pva.device_workspace_bytes(64, 1000, 1000, 32, 8) > small      # more sequences
+    assert pva.device_workspace_bytes(4, 100000, 1000, 32, 8) > small     # more query rows
+    assert pva.device_workspace_bytes(4, 1000, 4_000_000, 32, 8) > small  # more decode splits
+    with pytest.raises(ValueError):
+        pva.device_workspace_bytes(4, 1000, 1000, 32, 5)  # 5 does not divide 32
+
+
+@pytest.mark.parametrize("case,fragment", [
+    ("null_latch", "error latch"),
+    ("small_workspace", "workspace holds"),
+    ("misaligned", "256-byte aligned"),
+    ("bad_window", "local_window"),
+    ("bad_heads", "multiple of kv_num_heads"),
+])
+def test_device_entry_rejects_before_any_device_work(case, fragment):
+    lib = pva.load_library()
+    need = lib.varlen_attn_device_workspace_bytes(2, 64, 64, 8, 2, 128, 0, 2)
+    fake = ctypes.c_void_p(1 << 20)
+    ws, ws_bytes, latch, window, hkv = ctypes.c_void_p(1 << 20), need, fake, -1, 2
+    if case == "null_latch":
+        latch = None
+    elif case == "small_workspace":
+        ws_bytes = need - 256
+    elif case == "misaligned":
+        ws = ctypes.c_void_p((1 << 20) + 16)
+    elif case == "bad_window":
+        window = -3
+    elif case == "bad_heads":
+        hkv = 3
+    st = lib.varlen_attn_fwd_device(fake, fake, fake, fake, fake, 2, 64, 64, 8, hkv, 128, 0, 2, 0.0, 1, 0.0,
+                                    window, fake, ws, ws_bytes, latch, None)
+    msg = lib.varlen_attn_last_error().decode()
+    assert st == 1 and fragment in msg, (st, msg)
