@@ -25,9 +25,11 @@
 //      workspace);
 //   3. every thread writes items k = tid, tid + 1024, ..., finding the
 //      sequence of item k by binary search over those offsets.
-// Prefill items of a sequence run from its last row block to its first
-// (longest key range first). The decode list holds every full-chunk split
-// first and the shorter last splits after them, so that the last items
+// The prefill list takes the host scheduler's order: sequences by their
+// longest item (a bitonic sort in LDS; sequence order for batches too large
+// for it), each sequence's row blocks from the last to the first, head
+// groups innermost. The decode list holds every full-chunk split first and
+// the shorter last splits after them, longest first, so that the last items
 // handed to the GPU are the short ones.
 #include "common.h"
 
@@ -86,6 +88,28 @@ __device__ int32_t owner(const int32_t* off, int32_t n, int32_t k) {
   return lo;
 }
 
+// Sorts key[0, n) in descending order (n a power of two <= kLdsSeq), the
+// whole workgroup taking part.
+__device__ void bitonic_sort_desc(int64_t* key, int32_t n) {
+  const int tid = threadIdx.x;
+  for (int32_t k = 2; k <= n; k <<= 1) {
+    for (int32_t j = k >> 1; j > 0; j >>= 1) {
+      for (int32_t i = tid; i < n; i += kThreads) {
+        const int32_t ixj = i ^ j;
+        if (ixj > i) {
+          const int64_t a = key[i], c = key[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (a < c) : (a > c)) {
+            key[i] = c;
+            key[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // The split-KV key range of the single row of a decode sequence.
 struct DecRange {
   int32_t vb, ve, ns, nfull;
@@ -108,6 +132,8 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
   __shared__ int32_t s_q[kLdsSeq], s_kv[kLdsSeq];                    // cu arrays
   __shared__ int32_t s_pre[kLdsSeq], s_decf[kLdsSeq], s_decp[kLdsSeq];  // list offsets
   __shared__ int32_t s_cmb[kLdsSeq], s_part[kLdsSeq];
+  __shared__ int64_t s_key[kLdsSeq];   // prefill order of the sequences (LDS path)
+  __shared__ int64_t s_key2[kLdsSeq];  // order of the sequences' short last decode splits
   __shared__ int32_t s_err;
   __shared__ int32_t s_dchunk;
   __shared__ int64_t s_dec_keys;
@@ -181,7 +207,60 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
   const int32_t g_pre = dp.hq / dp.nh;      // head groups of a prefill item
   const int32_t g_dec = dp.hq / dp.nh_dec;  // head groups of a decode item
 
-  // ---- 2. per-sequence counts, one scan of all five -----------------------------
+  // ---- 2a. sequence orders (LDS path; sequence order for batches too large for
+  // it). Prefill: by the cost of the sequence's longest item, descending, ties
+  // by index (the host scheduler's order). Short last decode splits: by length,
+  // descending. key = value << 11 | (2047 - b).
+  const bool sorted = in_lds;
+  if (sorted) {
+    int32_t n = 1;
+    while (n < B) n <<= 1;
+    for (int32_t b = tid; b < n; b += kThreads) {
+      int64_t key = -1, key2 = -1;
+      if (b < B) {
+        int64_t top = 0, last = 0;
+        const int32_t lq = aq[b + 1] - aq[b];
+        const int32_t lkv = akv[b + 1] - akv[b];
+        if (lq > 0 && !(dp.use_decode && lq == 1)) {
+          // An item's key range never shrinks from one full row block to the
+          // next (causal) or never grows (window without causal), so the
+          // longest item is in the first, the second-to-last or the last
+          // (possibly short) row block.
+          const int32_t n_rb = (lq + dp.rows_per_item - 1) / dp.rows_per_item;
+          const int32_t cand[3] = {0, max(0, n_rb - 2), n_rb - 1};
+          for (int32_t ci = 0; ci < 3; ++ci) {
+            const int32_t rb = cand[ci];
+            const int32_t r0 = rb * dp.rows_per_item;
+            const int32_t rows = min(dp.rows_per_item, lq - r0);
+            const int32_t vb = visible_begin_dev(lq, lkv, r0, dp.window);
+            const int32_t ve = max(vb, visible_end_dev(lq, lkv, r0, rows, dp.causal));
+            top = max(top, (int64_t)(ve - vb) * rows);
+          }
+        } else if (lq == 1) {
+          const DecRange r = dec_range(lq, lkv, dp, dchunk);
+          last = (r.ve - r.vb) - (int64_t)r.nfull * dchunk;  // keys of the short last split
+        }
+        key = (top << 11) | (int64_t)(kLdsSeq - 1 - b);
+        key2 = (last << 11) | (int64_t)(kLdsSeq - 1 - b);
+      }
+      s_key[b] = key;
+      s_key2[b] = key2;
+    }
+    __syncthreads();
+    bitonic_sort_desc(s_key, n);
+    bitonic_sort_desc(s_key2, n);
+  }
+  // the sequence at position p of the prefill list order / of the decode
+  // list's short-split order
+  auto seq_at = [&](int32_t pos) -> int32_t {
+    return sorted ? (int32_t)(kLdsSeq - 1 - (s_key[pos] & (kLdsSeq - 1))) : pos;
+  };
+  auto seq_at2 = [&](int32_t pos) -> int32_t {
+    return sorted ? (int32_t)(kLdsSeq - 1 - (s_key2[pos] & (kLdsSeq - 1))) : pos;
+  };
+
+  // ---- 2b. per-sequence counts, one scan of all five ------------------------------
+  // (prefill counts are taken in prefill order, the others in sequence order)
   Counts base = {0, 0, 0, 0, 0};
   for (int32_t b0 = 0; b0 <= B; b0 += kThreads) {
     const int32_t b = b0 + tid;
@@ -193,14 +272,20 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
         if (dp.use_decode && lq == 1) {
           const DecRange r = dec_range(lq, lkv, dp, dchunk);
           n.decf = g_dec * r.nfull;
-          n.decp = g_dec * (r.ns - r.nfull);
           if (r.ns > 1) {
             n.cmb = g_dec;
             n.part = g_dec * r.ns * dp.nh_dec;
           }
-        } else {
-          n.pre = ((lq + dp.rows_per_item - 1) / dp.rows_per_item) * g_pre;
         }
+      }
+      const int32_t bp = seq_at(b);  // prefill counts in prefill order
+      const int32_t lqp = aq[bp + 1] - aq[bp];
+      if (lqp > 0 && !(dp.use_decode && lqp == 1)) n.pre = ((lqp + dp.rows_per_item - 1) / dp.rows_per_item) * g_pre;
+      const int32_t bd = seq_at2(b);  // short-split counts in their order
+      const int32_t lqd = aq[bd + 1] - aq[bd];
+      if (dp.use_decode && lqd == 1) {
+        const DecRange r = dec_range(lqd, akv[bd + 1] - akv[bd], dp, dchunk);
+        n.decp = g_dec * (r.ns - r.nfull);
       }
     }
     Counts tot;
@@ -257,8 +342,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     return it;
   };
   for (int32_t k = tid; k < base.pre; k += kThreads) {
-    const int32_t b = owner(apre, B, k);
-    const int32_t j = k - apre[b];
+    const int32_t pos = owner(apre, B, k);
+    const int32_t b = seq_at(pos);
+    const int32_t j = k - apre[pos];
     WorkItem it = proto(b, dp.prefill_kind);
     const int32_t n_rb = (it.len_q + dp.rows_per_item - 1) / dp.rows_per_item;
     const int32_t rb = n_rb - 1 - j / g_pre;  // last row block first
@@ -274,8 +360,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     const bool full = k < base.decf;
     const int32_t* off = full ? adecf : adecp;
     const int32_t kk = full ? k : k - base.decf;
-    const int32_t b = owner(off, B, kk);
-    const int32_t j = kk - off[b];
+    const int32_t pos = owner(off, B, kk);
+    const int32_t b = full ? pos : seq_at2(pos);
+    const int32_t j = kk - off[pos];
     WorkItem it = proto(b, kDecode);
     const DecRange r = dec_range(it.len_q, it.len_kv, dp, dchunk);
     const int32_t gi = full ? j / r.nfull : j;

@@ -357,15 +357,29 @@ varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
         }
       }
     }
-    // Longest first: the dispatcher hands out workgroups in index order, so
-    // this is the greedy longest-processing-time assignment over the CUs.
-    auto by_cost = [](const WorkItem& a, const WorkItem& b) {
-      const int64_t ca = (int64_t)(a.kv_end - a.kv_begin) * a.q_rows;
-      const int64_t cb = (int64_t)(b.kv_end - b.kv_begin) * b.q_rows;
-      return ca > cb;
-    };
-    std::stable_sort(plan.prefill.begin(), plan.prefill.end(), by_cost);
-    std::stable_sort(plan.decode.begin(), plan.decode.end(), by_cost);
+    // Item order. The dispatcher hands out workgroups in index order and
+    // deals them to the eight XCDs round-robin (index i to XCD i % 8).
+    // Prefill: sequences by their longest item first (most of the greedy
+    // longest-processing-time effect), then a sequence's row blocks from the
+    // last (longest key range) to the first, head groups innermost. Items i
+    // and i + 8 then read the same kv head's K/V over neighbouring row blocks
+    // of one sequence and run at about the same time on one XCD, so one L2
+    // serves both.
+    std::vector<int64_t> seq_top(pr.batch, 0);
+    for (const WorkItem& it : plan.prefill)
+      seq_top[it.seq] = std::max(seq_top[it.seq], (int64_t)(it.kv_end - it.kv_begin) * it.q_rows);
+    std::stable_sort(plan.prefill.begin(), plan.prefill.end(), [&](const WorkItem& a, const WorkItem& b) {
+      if (seq_top[a.seq] != seq_top[b.seq]) return seq_top[a.seq] > seq_top[b.seq];
+      if (a.seq != b.seq) return a.seq < b.seq;
+      if (a.q_row_begin != b.q_row_begin) return a.q_row_begin > b.q_row_begin;
+      if (a.kv_begin != b.kv_begin) return a.kv_begin < b.kv_begin;
+      return a.head_begin < b.head_begin;
+    });
+    // Split-KV decode: longest first (equal chunks, then the shorter last
+    // splits in decreasing length).
+    std::stable_sort(plan.decode.begin(), plan.decode.end(), [](const WorkItem& a, const WorkItem& b) {
+      return (int64_t)(a.kv_end - a.kv_begin) * a.q_rows > (int64_t)(b.kv_end - b.kv_begin) * b.q_rows;
+    });
   }
   return VARLEN_OK;
 }

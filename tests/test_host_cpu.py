@@ -263,12 +263,25 @@ def test_causal_tiles_never_start_above_the_frontier():
         assert kv1 == min(Lkv, last + Lkv - Lq + 1)
 
 
-def test_longest_items_first():
-    lq = [2048, 130, 900]
+def test_prefill_item_order():
+    """Sequences by their longest item first; within a sequence the row blocks
+    from the last to the first, the head groups of a row block adjacent (so
+    items i and i + 8 share a kv head's K/V on one XCD)."""
+    lq = [900, 2048, 130, 2048]
     _, items = pva.plan(_cu(lq), _cu(lq), 32, 8, is_causal=True, with_items=True)
     pre = items[items[:, 0] == KIND_PREFILL]
+    seqs = [int(b) for b in pre[:, 1]]
+    order = [b for i, b in enumerate(seqs) if i == 0 or seqs[i - 1] != b]
+    assert order == [1, 3, 0, 2]  # each sequence once, longest first, ties by index
+    for b in set(seqs):
+        mine = pre[pre[:, 1] == b]
+        r0 = mine[:, 2]
+        assert np.all(np.diff(r0) <= 0)
+        groups = len(set(mine[:, 4].tolist()))
+        assert groups == 8 and np.all(mine[:groups, 2] == mine[0, 2])
     cost = (pre[:, 7] - pre[:, 6]) * pre[:, 3]
-    assert np.all(np.diff(cost) <= 0)
+    assert cost[0] == cost.max()
+    assert pre[-1, 1] == 2 and pre[-1, 2] == 0  # the shortest sequence's first row block ends the list
 
 
 def test_workload_plans_fit():
