@@ -1,12 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of the packed varlen attention hot path on one MI355X.
 
-A step is one varlen_attn_fwd call over the full synthetic batch of a
-workload (argument validation, work scheduling, work-list upload and every
-kernel), with Q/K/V already resident in HBM. The default workload is the
-ragged causal prefill (B=16, L ~ U{128..2048}, Hq=32, Hkv=8, D=128, bf16).
+A step is one attention call over the full synthetic batch of a workload,
+with Q/K/V and the cu_seqlens arrays already resident in HBM. By default
+(--path graph) the call is varlen_attn_fwd_device captured once into a HIP
+graph, and a step is one replay: the device scheduler reads the cu arrays,
+validates them and builds the work list, then every attention kernel runs.
+--path device launches the same call eagerly each step; --path host times
+varlen_attn_fwd (host validation and scheduling, work-list upload, kernels).
+The default workload is the ragged causal prefill (B=16, L ~ U{128..2048},
+Hq=32, Hkv=8, D=128, bf16).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path graph|device|host]
 
 Prints ONE JSON line. ``value`` is valid-pair TFLOP/s (4 * pairs * Hq * D per
 step / step time) for prefill workloads and HBM GB/s (Q+K+V+O bytes per step
@@ -208,7 +213,7 @@ def main(argv=None) -> int:
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="measure the workload with a local window of W keys per row (W > 0); FLOPs count "
                          "only the pairs the window leaves visible")
-    ap.add_argument("--path", choices=["host", "device", "graph"], default="host",
+    ap.add_argument("--path", choices=["host", "device", "graph"], default="graph",
                     help="host: varlen_attn_fwd (host scheduler, host cu mirrors); device: "
                          "varlen_attn_fwd_device (device scheduler, no host work per call); graph: one "
                          "device-path call captured in a HIP graph, the timed steps are replays")
