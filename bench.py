@@ -13,8 +13,8 @@ Hq=32, Hkv=8, D=128, bf16).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path graph|device|host]
 
-Prints ONE JSON line. ``value`` is valid-pair TFLOP/s (4 * pairs * Hq * D per
-step / step time) for prefill workloads and HBM GB/s (Q+K+V+O bytes per step
+Prints ONE JSON line. ``value`` is valid-pair TFLOP/s (2 * pairs * Hq * (D + Dv)
+per step / step time) for prefill workloads and HBM GB/s (Q+K+V+O bytes per step
 / step time) for the decode workload. ``roofline`` reports the dominant
 kernel: its algorithmic work per launch over its average duration, timed with
 HIP events recorded by the library on the launch stream over the timed
@@ -129,7 +129,7 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0, window: int = 0):
     sub_keys = np.concatenate([keys[b] for b in seqs])
     n_all = int(cq[-1]) * w.num_heads
     perm = rng.permutation(n_all)
-    flops_per_row = 4.0 * sub_keys[perm // w.num_heads] * w.head_dim
+    flops_per_row = 2.0 * sub_keys[perm // w.num_heads] * (w.head_dim + w.dv)
     # calibrate on a growing slice (until it takes >= 1 s or covers every row),
     # then run a slice sized to the budget
     n_cal = min(n_all, 64)
@@ -157,7 +157,7 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0, window: int = 0):
     return {"value": float(flops_per_row[:n].sum() / dt / 1e12), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} random (token, head) rows of sequences {seqs} "
-                      f"({int(flops_per_row[:n].sum() / 4 / w.head_dim)} valid pairs), "
+                      f"({int(flops_per_row[:n].sum() / 2 / (w.head_dim + w.dv))} valid pairs), "
                       f"{reps} pass(es), {dt * reps:.1f} s"}
 
 
@@ -261,13 +261,13 @@ def main(argv=None) -> int:
     out = torch.empty(batch.total_q, w.num_heads, w.dv, dtype=batch.q.dtype, device="cuda:0")
     window = a.window if a.window > 0 else 0
     pairs = pva.valid_pairs(batch.cu_q, batch.cu_kv, w.is_causal, local_window=window or None)
-    flops = 4.0 * pairs * w.num_heads * w.head_dim
+    flops = 2.0 * pairs * w.num_heads * (w.head_dim + w.dv)
     el = 4 if w.dtype == "f32" else 2
     io_bytes = (batch.q.numel() + batch.k.numel() + batch.v.numel() + out.numel()) * el
     if window:
         # K and V rows no query row of its sequence can see are never read
         kv_rows = sum(b - max(0, b - a + 1 - window) if a else 0 for a, b in zip(batch.lq, batch.lkv))
-        io_bytes = (batch.q.numel() + out.numel()) * el + 2 * kv_rows * w.kv_num_heads * w.head_dim * el
+        io_bytes = (batch.q.numel() + out.numel()) * el + kv_rows * w.kv_num_heads * (w.head_dim + w.dv) * el
     stats, _ = pva.plan(batch.cu_q, batch.cu_kv, w.num_heads, w.kv_num_heads, head_dim=w.head_dim,
                         dtype=w.dtype, is_causal=w.is_causal, softcap=w.softcap, local_window=window or None)
     log(f"[bench] total_q={batch.total_q} total_kv={batch.total_kv} valid_pairs={pairs} plan={stats}")

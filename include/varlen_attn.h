@@ -102,9 +102,9 @@ typedef enum {
  *                 of dtype; every element is written
  *  stream         hipStream_t as void*
  *
- * GPU kernels exist for: bf16 and f16 with head_dim == v_head_dim in
- * {64, 128}; f32 with head_dim, v_head_dim <= 128. Anything else returns
- * VARLEN_ERR_UNSUPPORTED.
+ * GPU kernels exist for: bf16 and f16 with head_dim and v_head_dim each in
+ * {64, 128} (the two may differ); f32 with head_dim, v_head_dim <= 128.
+ * Anything else returns VARLEN_ERR_UNSUPPORTED.
  *
  * Buffers q, k, v, the cu arrays and out are borrowed and must stay valid
  * until the enqueued work completes. The library keeps a grow-only
@@ -267,8 +267,8 @@ varlen_status_t varlen_attn_plan(const int32_t* cu_seqlens_q_host,
  * Number of (query row, key) pairs the mask leaves visible for host cu
  * arrays ([PVA] "Causal alignment"): sum over sequences of L_q * L_kv, or
  * with is_causal of sum_i clamp(i + L_kv - L_q + 1, 0, L_kv). Returns -1 on
- * invalid arrays. The attention FLOPs of a call are 4 * pairs * Hq * D
- * (QK^T and P.V, 2 flops per multiply-add, D == Dv).
+ * invalid arrays. The attention FLOPs of a call are 2 * pairs * Hq * (D + Dv)
+ * (QK^T and P.V, 2 flops per multiply-add).
  */
 int64_t varlen_attn_valid_pairs(const int32_t* cu_seqlens_q_host,
                                 const int32_t* cu_seqlens_kv_host, int32_t batch,

@@ -316,7 +316,7 @@ def plan(cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None, head_di
 
 
 def valid_pairs(cu_seqlens_q, cu_seqlens_kv, is_causal: bool, local_window=None) -> int:
-    """Visible (query row, key) pairs; attention FLOPs are 4 * pairs * Hq * D."""
+    """Visible (query row, key) pairs; attention FLOPs are 2 * pairs * Hq * (D + Dv)."""
     lib = load_library()
     cq, ckv = _host_cu(cu_seqlens_q), _host_cu(cu_seqlens_kv)
     if local_window is None:

@@ -29,16 +29,16 @@
 
 namespace pva {
 
-template <int D, bool BF16, bool SOFTCAP>
+template <int D, int DV, bool BF16, bool SOFTCAP>
 __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* __restrict__ items) {
   constexpr int NW = 4;
   constexpr int BK = 32;            // keys per wave step
   constexpr int VSD = BK + 4;       // per-wave LDS V^T row stride (16-bit elements)
-  constexpr int DCH = D / 8;        // 16-byte chunks per key row
+  constexpr int DCH = DV / 8;       // 16-byte chunks per value row
   constexpr int VCH = BK * DCH / 64;  // V chunks per lane per step
-  constexpr int OS = D + 4;         // LDS row stride of the cross-wave O merge (floats)
+  constexpr int OS = DV + 4;        // LDS row stride of the cross-wave O merge (floats)
   static_assert(VCH * 64 == BK * DCH, "V block must split evenly over a wave");
-  constexpr int VT_BYTES = NW * D * VSD * 2;
+  constexpr int VT_BYTES = NW * DV * VSD * 2;
   constexpr int RED_BYTES = NW * 16 * OS * 4;
   constexpr int LDS_BYTES = VT_BYTES > RED_BYTES ? VT_BYTES : RED_BYTES;
 
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
   const int kv_end = it.kv_end;
   const int64_t tok = (int64_t)it.q_token0 + it.q_row_begin;
 
-  uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + wave * D * VSD;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(lds) + wave * DV * VSD;
 
   // Q fragments, the B operand of S^T = K Q^T: lane supplies head slot n at
   // head dims 32*kk + 8*grp + 0..7.
@@ -74,15 +74,16 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
     for (int kk = 0; kk < D / 32; ++kk) qf[kk] = slot_ok ? src[4 * kk + grp] : zero;
   }
 
-  f32x4_t oacc[D / 16];
+  f32x4_t oacc[DV / 16];
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) oacc[mb] = f32x4_t{};
+  for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] = f32x4_t{};
   float m_run = ninf();
   float l_run = 0.f;
 
-  const int64_t tok_stride = (int64_t)p.hkv * D;
+  const int64_t tok_stride = (int64_t)p.hkv * D;   // between consecutive key tokens
+  const int64_t v_stride = (int64_t)p.hkv * DV;    // between consecutive value tokens
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + ((int64_t)it.kv_token0 * p.hkv + g) * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + ((int64_t)it.kv_token0 * p.hkv + g) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + ((int64_t)it.kv_token0 * p.hkv + g) * DV;
 
   u32x4_t kf[2][D / 32];
   u32x4_t vr[VCH];
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
       const int key = chunk / DCH;
       const int d0 = (chunk % DCH) * 8;
       const int j = kb + key;
-      vr[c] = (j < kv_end) ? *reinterpret_cast<const u32x4_t*>(vbase + j * tok_stride + d0) : zero;
+      vr[c] = (j < kv_end) ? *reinterpret_cast<const u32x4_t*>(vbase + j * v_stride + d0) : zero;
     }
   };
 
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
     l_run = l_run * alpha + psum;
     m_run = m_new;
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb) oacc[mb] *= alpha;
+    for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] *= alpha;
     // P as the B operand over 32 keys: lane group grp holds keys 4grp + 0..3
     // (from sacc[0]) and 16 + 4grp + 0..3 (from sacc[1]).
     const u32x4_t pf = {pack2<BF16>(sacc[0][0], sacc[0][1]), pack2<BF16>(sacc[0][2], sacc[0][3]),
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int mb = 0; mb < D / 16; ++mb) {
+    for (int mb = 0; mb < DV / 16; ++mb) {
       const uint16_t* src = &vt[(16 * mb + n) * VSD + 4 * grp];
       const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
       const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 16);
@@ -218,13 +219,13 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
     red_l[wave][n] = l_w;
   }
 #pragma unroll
-  for (int mb = 0; mb < D / 16; ++mb) {
+  for (int mb = 0; mb < DV / 16; ++mb) {
     *reinterpret_cast<f32x4_t*>(&red_o[(wave * 16 + n) * OS + 16 * mb + 4 * grp]) = oacc[mb];
   }
   __syncthreads();
 
   // thread -> (head slot, 8 or 4 consecutive head dims)
-  constexpr int PER = D / 16;  // head dims per thread (16 threads per slot)
+  constexpr int PER = DV / 16;  // value dims per thread (16 threads per slot)
   const int slot = tid >> 4;
   const int d0 = (tid & 15) * PER;
   if (slot >= it.heads) return;
@@ -246,14 +247,14 @@ __global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* _
   const float inv = (wsum == 0.f) ? 0.f : 1.f / wsum;
   const int ohead = it.head_begin + slot;
   if (it.partial_base < 0) {
-    uint16_t* dst = static_cast<uint16_t*>(p.out) + (tok * p.hq + ohead) * D + d0;
+    uint16_t* dst = static_cast<uint16_t*>(p.out) + (tok * p.hq + ohead) * DV + d0;
 #pragma unroll
     for (int e = 0; e < PER; e += 2) {
       *reinterpret_cast<uint32_t*>(dst + e) = pack2<BF16>(acc[e] * inv, acc[e + 1] * inv);
     }
   } else {
     const int64_t pidx = partial_index(it, it.split, 0, slot);
-    float* po = p.part_o + pidx * D + d0;
+    float* po = p.part_o + pidx * DV + d0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) po[e] = acc[e] * inv;
     if ((tid & 15) == 0) p.part_lse[pidx] = (wsum == 0.f) ? ninf() : M + log2_fast(wsum);
@@ -301,17 +302,19 @@ hipError_t launch_decode(const Params& p, const WorkItem* items, int n, int dtyp
   if (n <= 0) return hipSuccess;
   const bool sc = p.softcap_on != 0;
   const bool bf = dtype == kBF16;
-#define PVA_DECODE(DD, BB, SS) \
-  hipLaunchKernelGGL((decode_kernel<DD, BB, SS>), dim3(n), dim3(256), 0, s, p, items)
-  if (p.d == 128) {
-    if (bf) { if (sc) PVA_DECODE(128, true, true); else PVA_DECODE(128, true, false); }
-    else { if (sc) PVA_DECODE(128, false, true); else PVA_DECODE(128, false, false); }
-  } else if (p.d == 64) {
-    if (bf) { if (sc) PVA_DECODE(64, true, true); else PVA_DECODE(64, true, false); }
-    else { if (sc) PVA_DECODE(64, false, true); else PVA_DECODE(64, false, false); }
-  } else {
-    return hipErrorInvalidValue;
-  }
+#define PVA_DECODE(DD, DVV, BB, SS) \
+  hipLaunchKernelGGL((decode_kernel<DD, DVV, BB, SS>), dim3(n), dim3(256), 0, s, p, items)
+#define PVA_DECODE_DV(DD, DVV)                                                  \
+  do {                                                                         \
+    if (bf) { if (sc) PVA_DECODE(DD, DVV, true, true); else PVA_DECODE(DD, DVV, true, false); }    \
+    else { if (sc) PVA_DECODE(DD, DVV, false, true); else PVA_DECODE(DD, DVV, false, false); }     \
+  } while (0)
+  if (p.d == 128 && p.dv == 128) PVA_DECODE_DV(128, 128);
+  else if (p.d == 64 && p.dv == 64) PVA_DECODE_DV(64, 64);
+  else if (p.d == 128 && p.dv == 64) PVA_DECODE_DV(128, 64);
+  else if (p.d == 64 && p.dv == 128) PVA_DECODE_DV(64, 128);
+  else return hipErrorInvalidValue;
+#undef PVA_DECODE_DV
 #undef PVA_DECODE
   return hipGetLastError();
 }

@@ -64,20 +64,31 @@ __device__ __forceinline__ int chunk_perm(int r) {
   }
 }
 
-template <int D, bool BF16, int NW, bool SOFTCAP>
+// Tile geometry of one operand with rows of W 16-bit elements: a wave's 1 KB
+// load covers 512 / W key rows, a 64-key tile splits into 1 KB blocks dealt
+// round-robin to the NW waves.
+template <int W, int NW>
+struct TileShape {
+  static constexpr int BN = 64;
+  static constexpr int CH = W / 8;               // 16-byte chunks per key row
+  static constexpr int TILE = BN * W;            // 16-bit elements per tile
+  static constexpr int ROWS_PER_BLOCK = 512 / W;
+  static constexpr int BLOCKS = BN / ROWS_PER_BLOCK;
+  static constexpr int BPW = BLOCKS / NW;        // 1 KB blocks per wave per tile
+  static_assert(BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
+};
+
+template <int D, int DV, bool BF16, int NW, bool SOFTCAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
-  constexpr int BN = 64;                   // keys per tile
-  constexpr int DCH = D / 8;               // 16-byte chunks per key row
-  constexpr int TILE = BN * D;             // 16-bit elements per K (or V) tile
-  constexpr int ROWS_PER_BLOCK = 512 / D;  // key rows per 1 KB wave load
-  constexpr int BLOCKS = BN / ROWS_PER_BLOCK;
-  constexpr int BPW = BLOCKS / NW;         // 1 KB blocks per wave per tile (K and V each)
-  static_assert(BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
+  constexpr int BN = 64;  // keys per tile
+  using KS = TileShape<D, NW>;
+  using VS = TileShape<DV, NW>;
 
   // K0 K1 V0 V1, each [key][d] with 16-byte chunk c of row r stored at chunk
-  // c ^ chunk_perm<D>(r).
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];
+  // c ^ chunk_perm<row width>(r).
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * KS::TILE + 2 * VS::TILE];
+  constexpr int V0 = 2 * KS::TILE;  // first V buffer
 
   if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
   const WorkItem it = items[blockIdx.x];
@@ -117,51 +128,52 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = row_ok ? src[2 * kk + half] : zero;
   }
 
-  f32x16_t oacc[D / 32];
+  f32x16_t oacc[DV / 32];
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
+  for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = f32x16_t{};
   float m_ref = ninf();  // reference max of the row (log2 units)
   float l_run = 0.f;     // this lane's half of the row sum
 
   // ---- HBM -> LDS tile loads ------------------------------------------------
   // Wave w fills 1 KB blocks w, w + NW, ... of each tile; lane L of a block
-  // lands at byte 16*L of it, i.e. row L / DCH of the block, stored chunk
-  // L % DCH, so it fetches logical chunk (L % DCH) ^ chunk_perm<D>(row).
-  const int64_t tok_stride = (int64_t)p.hkv * D;  // elements between consecutive tokens
+  // lands at byte 16*L of it, i.e. row L / CH of the block, stored chunk
+  // L % CH, so it fetches logical chunk (L % CH) ^ chunk_perm(row).
+  const int64_t k_stride = (int64_t)p.hkv * D;   // elements between consecutive tokens
+  const int64_t v_stride = (int64_t)p.hkv * DV;
   const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.k) +
                                                     ((int64_t)it.kv_token0 * p.hkv + g) * D);
   const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) +
-                                                    ((int64_t)it.kv_token0 * p.hkv + g) * D);
-  const int blk_row = wave * ROWS_PER_BLOCK + lane / DCH;  // row in the first block of this wave
-  const int dma_chunk = (lane % DCH) ^ chunk_perm<D>(blk_row);  // same for every block of the wave
-  const uint32_t dma_off = (uint32_t)((blk_row * tok_stride + dma_chunk * 8) * 2);
-  const uint32_t dma_step = (uint32_t)(NW * ROWS_PER_BLOCK * tok_stride * 2);  // bytes between this wave's blocks
+                                                    ((int64_t)it.kv_token0 * p.hkv + g) * DV);
+  const int k_row = wave * KS::ROWS_PER_BLOCK + lane / KS::CH;  // row in this wave's first K block
+  const int v_row = wave * VS::ROWS_PER_BLOCK + lane / VS::CH;
+  const uint32_t k_off = (uint32_t)((k_row * k_stride + ((lane % KS::CH) ^ chunk_perm<D>(k_row)) * 8) * 2);
+  const uint32_t v_off = (uint32_t)((v_row * v_stride + ((lane % VS::CH) ^ chunk_perm<DV>(v_row)) * 8) * 2);
+  const uint32_t k_step = (uint32_t)(NW * KS::ROWS_PER_BLOCK * k_stride * 2);  // bytes between this wave's blocks
+  const uint32_t v_step = (uint32_t)(NW * VS::ROWS_PER_BLOCK * v_stride * 2);
 
   auto issue_tile = [&](int kt, int buf) {
-    const char* kb = kbase + (int64_t)kt * tok_stride * 2;
-    const char* vb = vbase + (int64_t)kt * tok_stride * 2;
-    uint16_t* kl = lds + buf * TILE + wave * 512;
-    uint16_t* vl = lds + (2 + buf) * TILE + wave * 512;
+    const char* kb = kbase + (int64_t)kt * k_stride * 2;
+    const char* vb = vbase + (int64_t)kt * v_stride * 2;
+    uint16_t* kl = lds + buf * KS::TILE + wave * 512;
+    uint16_t* vl = lds + V0 + buf * VS::TILE + wave * 512;
     const int rows = kv_end - kt;
-    if (rows >= BN) {
+    // rows at or past kv_end are zeros (never the next sequence)
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        lds_dma16_async(kb + dma_off + i * dma_step, lds_addr32(kl + i * NW * 512));
-        lds_dma16_async(vb + dma_off + i * dma_step, lds_addr32(vl + i * NW * 512));
+    for (int i = 0; i < KS::BPW; ++i) {
+      if (rows >= BN || k_row + i * NW * KS::ROWS_PER_BLOCK < rows) {
+        lds_dma16_async(kb + k_off + i * k_step, lds_addr32(kl + i * NW * 512));
+      } else {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(kl + i * NW * 512 + 8 * lane) = zero;
       }
-    } else {
-      // last tile: rows at or past kv_end are zeros (never the next sequence)
+    }
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        const int r = blk_row + i * NW * ROWS_PER_BLOCK;
-        if (r < rows) {
-          lds_dma16_async(kb + dma_off + i * dma_step, lds_addr32(kl + i * NW * 512));
-          lds_dma16_async(vb + dma_off + i * dma_step, lds_addr32(vl + i * NW * 512));
-        } else {
-          const u32x4_t zero = {0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4_t*>(kl + i * NW * 512 + 8 * lane) = zero;
-          *reinterpret_cast<u32x4_t*>(vl + i * NW * 512 + 8 * lane) = zero;
-        }
+    for (int i = 0; i < VS::BPW; ++i) {
+      if (rows >= BN || v_row + i * NW * VS::ROWS_PER_BLOCK < rows) {
+        lds_dma16_async(vb + v_off + i * v_step, lds_addr32(vl + i * NW * 512));
+      } else {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(vl + i * NW * 512 + 8 * lane) = zero;
       }
     }
   };
@@ -176,12 +188,12 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const int trg = lane >> 4;
   const int tr_i = lane & 15;
   const int tr_key = 4 * (trg >> 1) + (tr_i >> 2);
-  int v_addr[D / 32], v_addr8[D / 32];  // rows tr_key and tr_key + 8 of each 16-key block
+  int v_addr[DV / 32], v_addr8[DV / 32];  // rows tr_key and tr_key + 8 of each 16-key block
 #pragma unroll
-  for (int mb = 0; mb < D / 32; ++mb) {
+  for (int mb = 0; mb < DV / 32; ++mb) {
     const int dd = 32 * mb + 16 * (trg & 1) + 4 * (tr_i & 3);
-    v_addr[mb] = tr_key * D + (((dd >> 3) ^ chunk_perm<D>(tr_key)) << 3) + (dd & 7);
-    v_addr8[mb] = (tr_key + 8) * D + (((dd >> 3) ^ chunk_perm<D>(tr_key + 8)) << 3) + (dd & 7);
+    v_addr[mb] = tr_key * DV + (((dd >> 3) ^ chunk_perm<DV>(tr_key)) << 3) + (dd & 7);
+    v_addr8[mb] = (tr_key + 8) * DV + (((dd >> 3) ^ chunk_perm<DV>(tr_key + 8)) << 3) + (dd & 7);
   }
 
   // One key tile. MODE selects the masking and the softmax bookkeeping:
@@ -198,8 +210,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   auto compute = [&](int buf, int kt, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr bool MASK = MODE != kPlain;
-    const uint16_t* ks = lds + buf * TILE;
-    const uint16_t* vs = lds + (2 + buf) * TILE;
+    const uint16_t* ks = lds + buf * KS::TILE;
+    const uint16_t* vs = lds + V0 + buf * VS::TILE;
 
     // ---- S^T = K Q^T -------------------------------------------------------
     // K fragments stream through a ring of KPF register slots, KPF - 1 steps
@@ -261,7 +273,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
         m_ref = m_new;
         l_run *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) oacc[mb] *= alpha;
+        for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] *= alpha;
       }
     }
     if constexpr (MODE == kPlain || MODE == kMasked) {
@@ -329,15 +341,15 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
     for (int kb = 0; kb < BN / 16; ++kb) {
-      u32x4_t a[D / 32];
+      u32x4_t a[DV / 32];
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) {
-        const u32x2_t lo = lds_read_tr16(vs + v_addr[mb] + 16 * kb * D);
-        const u32x2_t hi = lds_read_tr16(vs + v_addr8[mb] + 16 * kb * D);
+      for (int mb = 0; mb < DV / 32; ++mb) {
+        const u32x2_t lo = lds_read_tr16(vs + v_addr[mb] + 16 * kb * DV);
+        const u32x2_t hi = lds_read_tr16(vs + v_addr8[mb] + 16 * kb * DV);
         a[mb] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
       }
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = mfma32<BF16>(a[mb], pf[kb], oacc[mb]);
+      for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = mfma32<BF16>(a[mb], pf[kb], oacc[mb]);
     }
   };
 
@@ -403,14 +415,14 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   {
     float chk = sum_with_partner32(l_run);
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
+    for (int mb = 0; mb < DV / 32; ++mb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) chk = __builtin_fmaf(oacc[mb][r], 0.f, chk);
     }
     const bool bad = wave_active && row_ok && !__builtin_isfinite(chk);
     if (__syncthreads_or(__any(bad) ? 1 : 0)) {
 #pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb) oacc[mb] = f32x16_t{};
+      for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = f32x16_t{};
       m_ref = ninf();
       l_run = 0.f;
       run_pass(std::true_type{});
@@ -422,9 +434,9 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const float l_tot = sum_with_partner32(l_run);
   const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
   if (it.partial_base < 0) {
-    uint16_t* dst = static_cast<uint16_t*>(p.out) + (tok * p.hq + head) * D;
+    uint16_t* dst = static_cast<uint16_t*>(p.out) + (tok * p.hq + head) * DV;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
+    for (int mb = 0; mb < DV / 32; ++mb) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int d = 32 * mb + 8 * u + 4 * half;
@@ -435,9 +447,9 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     }
   } else {
     const int64_t pidx = partial_index(it, it.split, my_row, hh);
-    float* po = p.part_o + pidx * D;
+    float* po = p.part_o + pidx * DV;
 #pragma unroll
-    for (int mb = 0; mb < D / 32; ++mb) {
+    for (int mb = 0; mb < DV / 32; ++mb) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int d = 32 * mb + 8 * u + 4 * half;
@@ -450,32 +462,38 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   }
 }
 
-template <int D, bool BF16, int NW>
+template <int D, int DV, bool BF16, int NW>
 static hipError_t launch_nw(const Params& p, const WorkItem* items, int n, bool softcap,
                             hipStream_t s) {
   if (softcap) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, BF16, NW, true>), dim3(n), dim3(NW * 64), 0, s, p, items);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, DV, BF16, NW, true>), dim3(n), dim3(NW * 64), 0, s, p, items);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, BF16, NW, false>), dim3(n), dim3(NW * 64), 0, s, p, items);
+    hipLaunchKernelGGL((prefill_mfma_kernel<D, DV, BF16, NW, false>), dim3(n), dim3(NW * 64), 0, s, p, items);
   }
   return hipGetLastError();
 }
 
-template <int D, bool BF16>
+template <int D, int DV, bool BF16>
 static hipError_t launch_d(const Params& p, const WorkItem* items, int n, int nw, bool softcap,
                            hipStream_t s) {
-  return nw == 8 ? launch_nw<D, BF16, 8>(p, items, n, softcap, s)
-                 : launch_nw<D, BF16, 4>(p, items, n, softcap, s);
+  return nw == 8 ? launch_nw<D, DV, BF16, 8>(p, items, n, softcap, s)
+                 : launch_nw<D, DV, BF16, 4>(p, items, n, softcap, s);
+}
+
+template <bool BF16>
+static hipError_t launch_t(const Params& p, const WorkItem* items, int n, int nw, bool softcap, hipStream_t s) {
+  if (p.d == 128 && p.dv == 128) return launch_d<128, 128, BF16>(p, items, n, nw, softcap, s);
+  if (p.d == 64 && p.dv == 64) return launch_d<64, 64, BF16>(p, items, n, nw, softcap, s);
+  if (p.d == 128 && p.dv == 64) return launch_d<128, 64, BF16>(p, items, n, nw, softcap, s);
+  if (p.d == 64 && p.dv == 128) return launch_d<64, 128, BF16>(p, items, n, nw, softcap, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_mfma(const Params& p, const WorkItem* items, int n, int dtype, int nw,
                                hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const bool sc = p.softcap_on != 0;
-  const bool bf = dtype == kBF16;
-  if (p.d == 128) return bf ? launch_d<128, true>(p, items, n, nw, sc, s) : launch_d<128, false>(p, items, n, nw, sc, s);
-  if (p.d == 64) return bf ? launch_d<64, true>(p, items, n, nw, sc, s) : launch_d<64, false>(p, items, n, nw, sc, s);
-  return hipErrorInvalidValue;
+  return dtype == kBF16 ? launch_t<true>(p, items, n, nw, sc, s) : launch_t<false>(p, items, n, nw, sc, s);
 }
 
 }  // namespace pva

@@ -148,8 +148,8 @@ varlen_status_t check_supported(const Problem& pr) {
       return fail(VARLEN_ERR_UNSUPPORTED, "f32 supports head_dim and v_head_dim <= 128, got %d and %d", pr.d, pr.dv);
     return VARLEN_OK;
   }
-  if (pr.d != pr.dv || (pr.d != 64 && pr.d != 128))
-    return fail(VARLEN_ERR_UNSUPPORTED, "f16/bf16 support head_dim == v_head_dim in {64, 128}, got %d and %d", pr.d,
+  if ((pr.d != 64 && pr.d != 128) || (pr.dv != 64 && pr.dv != 128))
+    return fail(VARLEN_ERR_UNSUPPORTED, "f16/bf16 support head_dim and v_head_dim in {64, 128}, got %d and %d", pr.d,
                 pr.dv);
   return VARLEN_OK;
 }

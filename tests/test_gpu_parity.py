@@ -23,8 +23,8 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _workload(dtype="bf16", hq=8, hkv=2, d=128, causal=True, softcap=0.0, scale=0.0, sigma=1.0, seed=11):
-    return synth.Workload("custom", 0, hq, hkv, d, dtype, causal, softcap, scale, sigma, seed)
+def _workload(dtype="bf16", hq=8, hkv=2, d=128, causal=True, softcap=0.0, scale=0.0, sigma=1.0, seed=11, dv=None):
+    return synth.Workload("custom", 0, hq, hkv, d, dtype, causal, softcap, scale, sigma, seed, dv)
 
 
 def _batch(w, lq, lkv):
@@ -269,6 +269,40 @@ def test_back_to_back_calls_on_two_streams():
             assert torch.equal(outs[r][i], alone[i]), (r, i)
 
 
+# Value head size different from the query/key head size (v_head_size is
+# its own input dimension: packed_varlen_attention.rs page, "Schema (v1)").
+DV_CASES = [
+    # (name, workload kwargs, lq, lkv, local window, options)
+    ("bf16_d128_dv64_causal", dict(hq=8, hkv=2, dv=64), [70, 1, 129, 33, 0, 200], [70, 1, 129, 33, 5, 200], None, {}),
+    ("bf16_d64_dv128_causal", dict(hq=8, hkv=2, d=64, dv=128), [70, 1, 129, 33], [70, 900, 129, 40], None, {}),
+    ("bf16_d128_dv64_noncausal_mha", dict(hq=4, hkv=4, causal=False, dv=64), [77, 128, 5], [31, 128, 200], None, {}),
+    ("f16_d64_dv128_softcap", dict(dtype="f16", hq=16, hkv=2, d=64, dv=128, softcap=20.0, sigma=1.5),
+     [150, 64, 1], [150, 64, 900], None, {}),
+    ("f16_d128_dv64_tail_aligned", dict(dtype="f16", hq=8, hkv=2, dv=64), [40, 3, 100, 1], [300, 90, 100, 17],
+     None, {}),
+    ("bf16_d128_dv64_decode_split", dict(hq=16, hkv=2, dv=64, softcap=20.0), [1, 100, 1, 257, 1],
+     [1000, 700, 129, 300, 5], None, dict(decode_chunk=128)),
+    ("bf16_d64_dv128_decode_split", dict(hq=16, hkv=2, d=64, dv=128), [1, 1, 1, 100], [3000, 500, 800, 1000],
+     None, dict(decode_chunk=256)),
+    ("bf16_d64_dv128_prefill_split", dict(hq=8, hkv=2, d=64, dv=128), [257, 100], [900, 1000], None,
+     dict(prefill_kv_chunk=128)),
+    ("bf16_d128_dv64_window", dict(hq=8, hkv=2, dv=64), [40, 3, 100, 1], [300, 90, 100, 1700], 64, {}),
+    ("bf16_d64_dv128_prefill_only", dict(hq=8, hkv=2, d=64, dv=128), [1, 64, 1], [500, 64, 91], None,
+     dict(decode_path=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw,lq,lkv,window,opts", DV_CASES, ids=[c[0] for c in DV_CASES])
+def test_value_head_size_differs(name, kw, lq, lkv, window, opts):
+    w = _workload(**kw)
+    _say(name, w, lq, lkv, "window", window, opts)
+    batch = _batch(w, lq, lkv)
+    got = run_gpu(batch, local_window=window, **opts).double().cpu().numpy().reshape(
+        batch.total_q, w.num_heads, w.dv)
+    ma, rel = compare(got, oracle_all(batch, local_window=window or 0), w.dtype)
+    _say(name, "max_abs", ma, "rel_l2", rel)
+
+
 # Local window (page src/kernels/attention.rs, softmax kernel local_min; page
 # src/kernels/group_query_attention.rs, local_window_size): each case against
 # the oracle with the same window.
@@ -357,6 +391,8 @@ DEVICE = [
     ("bf16_mha_rows4", dict(hq=2, hkv=2, causal=False), [300, 77], [300, 900], None),
     ("f16_gqa8", dict(dtype="f16", hq=16, hkv=2), [150, 64, 1], [150, 64, 900], None),
     ("bf16_d64", dict(hq=8, hkv=2, d=64), [100, 1, 37], [100, 513, 37], None),
+    ("bf16_d128_dv64", dict(hq=8, hkv=2, dv=64), [1, 100, 1, 257], [3000, 700, 129, 300], None),
+    ("f16_d64_dv128_window", dict(dtype="f16", hq=8, hkv=2, d=64, dv=128), [40, 1, 100], [300, 2000, 100], 48),
     ("f32_gqa", dict(dtype="f32", hq=8, hkv=2, d=64), [70, 1, 33], [70, 200, 40], None),
 ]
 

@@ -77,7 +77,8 @@ def _fwd_status(cu_q, cu_kv, hq=4, hkv=2, d=64, dv=0, dtype=2, scale=0.0, causal
     (dict(batch=0), 2, "batch must be >= 1"),
     (dict(total_q=11), 2, "must equal the packed token count"),
     (dict(d=96), 3, "f16/bf16 support head_dim"),
-    (dict(d=128, dv=64), 3, "f16/bf16 support head_dim"),
+    (dict(d=128, dv=96), 3, "f16/bf16 support head_dim"),
+    (dict(d=32, dv=64), 3, "f16/bf16 support head_dim"),
     (dict(dtype=0, d=256), 3, "f32 supports"),
     (dict(ptr=0), 1, "must be non-null"),
 ])
