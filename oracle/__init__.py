@@ -25,6 +25,10 @@ page src/kernels/standard_attention.rs, "Semantics"):
   local_window_size attribute);
 * stable softmax over the visible keys, rows with no visible key are zero;
 * ``out = softmax . V`` in fp64.
+
+``rope_append`` (numpy, fp64) is the oracle of the step before decode: the
+rotary embedding of new query/key rows and their append to a fixed-capacity
+KV cache.
 """
 from __future__ import annotations
 

@@ -167,3 +167,72 @@ def workload_batch(name: str, device="cpu") -> Batch:
     w = WORKLOADS[name]
     lq, lkv = draw_lengths(name)
     return make_batch(w, lq, lkv, device=device)
+
+
+# ---------------------------------------------------------------------------
+# Decode-side inputs: new rows for a fixed-capacity KV cache, and rotary tables.
+# ---------------------------------------------------------------------------
+def rotary_tables(rows: int, rotary_dim: int, base: float = 10000.0, device="cpu"):
+    """cos and sin tables [rows, rotary_dim / 2] in fp32 for the usual rotary
+    frequencies base^(-2m / rotary_dim) at positions 0 .. rows - 1 (an input of
+    the rotary step, computed in fp64 and rounded to fp32)."""
+    import torch
+    m = np.arange(rotary_dim // 2, dtype=np.float64)
+    inv = base ** (-2.0 * m / rotary_dim)
+    ang = np.arange(rows, dtype=np.float64)[:, None] * inv[None, :]
+    cos = torch.from_numpy(np.cos(ang).astype(np.float32))
+    sin = torch.from_numpy(np.sin(ang).astype(np.float32))
+    return cos.to(device), sin.to(device)
+
+
+@dataclasses.dataclass
+class CacheStep:
+    """New rows of a packed batch and a fixed-capacity cache they append to.
+
+    Sequence b owns cache rows [b * capacity, (b + 1) * capacity); its first
+    past[b] rows hold earlier tokens (seeded normals) and the rest hold NaN,
+    so that a read of a slot that holds no token shows in the result."""
+    workload: Workload
+    lq: list
+    past: list
+    capacity: int
+    cu_q: np.ndarray
+    q: object        # [total_q, Hq, D]
+    k: object        # [total_q, Hkv, D]
+    v: object        # [total_q, Hkv, Dv]
+    k_cache: object  # [batch * capacity, Hkv, D]
+    v_cache: object  # [batch * capacity, Hkv, Dv]
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q[-1])
+
+    @property
+    def kv_len(self) -> list:
+        return [p + n for p, n in zip(self.past, self.lq)]
+
+
+def make_cache_step(w: Workload, lq, past, capacity: int, device="cpu", seed: Optional[int] = None) -> CacheStep:
+    s = w.seed if seed is None else seed
+    cu_q = cu_seqlens(lq)
+    tq = int(cu_q[-1])
+    bsz = len(lq)
+    q = normal_tensor((tq, w.num_heads, w.head_dim), w.dtype, w.sigma, s, 0, device)
+    k = normal_tensor((tq, w.kv_num_heads, w.head_dim), w.dtype, w.sigma, s, 1, device)
+    v = normal_tensor((tq, w.kv_num_heads, w.dv), w.dtype, w.sigma, s, 2, device)
+    kc = normal_tensor((bsz * capacity, w.kv_num_heads, w.head_dim), w.dtype, w.sigma, s, 3, device)
+    vc = normal_tensor((bsz * capacity, w.kv_num_heads, w.dv), w.dtype, w.sigma, s, 4, device)
+    for b in range(bsz):
+        kc[b * capacity + past[b]:(b + 1) * capacity] = float("nan")
+        vc[b * capacity + past[b]:(b + 1) * capacity] = float("nan")
+    return CacheStep(w, list(lq), list(past), capacity, cu_q, q, k, v, kc, vc)
+
+
+def decode_cache_step(device="cpu") -> CacheStep:
+    """The packed decode workload as one decode step over a cache: each
+    sequence appends its one new row after L_kv - 1 cached rows; the capacity
+    is the longest L_kv rounded up to 256 rows."""
+    w = WORKLOADS["packed_decode"]
+    lq, lkv = draw_lengths("packed_decode")
+    cap = (max(lkv) + 255) // 256 * 256
+    return make_cache_step(w, lq, [n - 1 for n in lkv], cap, device=device)
