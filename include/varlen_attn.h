@@ -221,6 +221,99 @@ varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void*
                                        int32_t* error_latch, void* stream);
 
 /*
+ * varlen_kv_append_rope -- the step before a decode (or chunked-prefill) call
+ * over a fixed-capacity KV cache: rotary position embedding of the new query
+ * and key rows, and the append of the new key and value rows into the cache,
+ * in one launch (page src/kernels/group_query_attention.rs: the rotary kernel
+ * gqa_rope_bnsh, the cache kernels gqa_build_cache / gqa_append_cache and the
+ * fused single-token prep gqa_fuse_decode_prep; page src/kernels/attention.rs,
+ * the fixed-capacity, fixed-slot append test). Capture-safe like
+ * varlen_attn_fwd_device: it only enqueues one kernel on `stream`.
+ *
+ * Rows are packed by cu_seqlens_q as in varlen_attn_fwd. The cache keeps the
+ * attention's row format: k_cache [batch * cache_capacity, Hkv, D] and
+ * v_cache [batch * cache_capacity, Hkv, Dv], sequence b owning rows
+ * [b * cache_capacity, (b + 1) * cache_capacity), of which the first
+ * cache_seqlens[b] hold earlier tokens.
+ *
+ *  q, q_out       device [total_q rows, q_row_stride] new query rows and
+ *                 dense [total_q, Hq, D] rotated output; q_out may equal q
+ *                 (in place, dense rows only); both NULL: no query work
+ *  k, v           device new key / value rows, k_row_stride / v_row_stride
+ *                 elements apart (0: dense, Hkv*D and Hkv*Dv). A packed QKV
+ *                 buffer [total_q, (Hq + 2 Hkv) * D] is passed as q = base,
+ *                 k = base + Hq*D, v = base + (Hq + Hkv)*D with all three
+ *                 strides (Hq + 2 Hkv) * D
+ *  k_cache, v_cache  device caches as above; new row i of sequence b goes
+ *                 to row b * cache_capacity + cache_seqlens[b] + i; no other
+ *                 cache row is written
+ *  cu_seqlens_q   device int32 [batch + 1]
+ *  cache_seqlens  device int32 [batch], tokens already in each sequence
+ *  kv_seqlens_out device int32 [batch] or NULL; receives cache_seqlens[b] +
+ *                 L_q[b], the key count of the attention call over the cache
+ *  cos_cache, sin_cache  device fp32 [rotary_rows, rotary_dim / 2]
+ *  position_ids   device int64 [total_q] or NULL; the position of each new
+ *                 row (default cache_seqlens[b] + i)
+ *  rotary_dim     0: no rotation (a plain append); else even in [2, D]. Pair
+ *                 m < rotary_dim/2 of every query and key head is dims
+ *                 (2m, 2m+1) if rotary_interleaved, else (m, m +
+ *                 rotary_dim/2); it turns by the table angle at the row's
+ *                 position: (a, b) -> (a*cos - b*sin, a*sin + b*cos). Dims
+ *                 from rotary_dim on are copied. Values are never turned.
+ *  dtype          storage type of q, k, v, q_out and the caches; the rotation
+ *                 is worked in fp32 and rounded to nearest even
+ *  error_latch    as varlen_attn_fwd_device (the same word can serve both
+ *                 calls). Bits: 1/2/4 cu_seqlens_q as there, 128
+ *                 cache_seqlens[b] < 0, 256 cache_seqlens[b] + L_q[b] >
+ *                 cache_capacity, 512 a position outside [0, rotary_rows).
+ *                 A row whose sequence or position is invalid writes
+ *                 nothing; a workgroup that finds the latch already set
+ *                 writes nothing, so after an error the step's outputs are
+ *                 unspecified (and the attention call that follows computes
+ *                 nothing until the latch is cleared).
+ *
+ * Requires D and Dv even, batch * cache_capacity < 2^31. Buffers are
+ * borrowed; nothing is allocated.
+ */
+varlen_status_t varlen_kv_append_rope(const void* q, void* q_out, const void* k, const void* v,
+                                      int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
+                                      void* k_cache, void* v_cache, const int32_t* cu_seqlens_q,
+                                      const int32_t* cache_seqlens, int32_t* kv_seqlens_out,
+                                      const float* cos_cache, const float* sin_cache,
+                                      const int64_t* position_ids, int32_t batch, int64_t total_q,
+                                      int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                      int32_t v_head_dim, int32_t dtype, int32_t cache_capacity,
+                                      int32_t rotary_dim, int32_t rotary_rows, int32_t rotary_interleaved,
+                                      int32_t* error_latch, void* stream);
+
+/*
+ * varlen_attn_fwd_kvcache -- varlen_attn_fwd_device with the keys and values
+ * in a fixed-capacity cache instead of packed by cu_seqlens_kv: sequence b
+ * attends to cache rows [b * cache_capacity, b * cache_capacity +
+ * kv_seqlens[b]) (the attention read is bounded to the valid rows; the rest
+ * of the cache is never read, per the fixed-capacity append path of page
+ * src/kernels/attention.rs). The causal mask stays tail-aligned: query row i
+ * of sequence b sees key j <= i + kv_seqlens[b] - L_q[b].
+ *
+ *  k_cache, v_cache  device [batch * cache_capacity, Hkv, D] / [..., Dv]
+ *  kv_seqlens     device int32 [batch] (e.g. kv_seqlens_out of
+ *                 varlen_kv_append_rope); a length < 0 or > cache_capacity
+ *                 sets bit 1024 of the latch
+ *  workspace      at least varlen_attn_device_workspace_bytes(batch,
+ *                 total_q, batch * cache_capacity, ...) bytes
+ *
+ * Everything else as varlen_attn_fwd_device (bits 8/16/32 are not used).
+ */
+varlen_status_t varlen_attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* cu_seqlens_q, const int32_t* kv_seqlens,
+                                        int32_t batch, int64_t total_q, int32_t cache_capacity,
+                                        int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                        int32_t v_head_dim, int32_t dtype, float scale,
+                                        int32_t is_causal, float softcap, int32_t local_window,
+                                        void* out, void* workspace, size_t workspace_bytes,
+                                        int32_t* error_latch, void* stream);
+
+/*
  * varlen_attn_plan -- the host-side work scheduler on its own (no device
  * work, no HIP call; usable without a GPU). It validates like
  * varlen_attn_fwd (with host cu arrays) and fills `stats` with what a call
@@ -289,10 +382,11 @@ int64_t varlen_attn_valid_pairs_window(const int32_t* cu_seqlens_q_host,
  * adds their elapsed times to per-kernel totals and returns the totals since
  * the last enable. Index k of the arrays: 0 prefill (MFMA), 1 prefill
  * (fp32), 2 split-KV decode, 3 combine, 4 work-list upload, 5 device
- * scheduler (varlen_attn_fwd_device).
+ * scheduler (varlen_attn_fwd_device, varlen_attn_fwd_kvcache), 6 cache step
+ * (varlen_kv_append_rope).
  * varlen_attn_profile_enable(0) stops recording; (1) clears and starts.
  */
-#define VARLEN_PROFILE_KINDS 6
+#define VARLEN_PROFILE_KINDS 7
 typedef struct {
   double total_ms[VARLEN_PROFILE_KINDS];
   int64_t launches[VARLEN_PROFILE_KINDS];

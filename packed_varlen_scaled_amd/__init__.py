@@ -59,16 +59,18 @@ class PlanStats(ctypes.Structure):
 
 
 class ProfileTotals(ctypes.Structure):
-    _fields_ = [("total_ms", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6),
-                ("items", ctypes.c_int64 * 6)]
+    _fields_ = [("total_ms", ctypes.c_double * 7), ("launches", ctypes.c_int64 * 7),
+                ("items", ctypes.c_int64 * 7)]
 
 
-PROFILE_KINDS = ("prefill_mfma", "prefill_f32", "decode", "combine", "upload", "device_plan")
+PROFILE_KINDS = ("prefill_mfma", "prefill_f32", "decode", "combine", "upload", "device_plan", "cache_step")
 
 # Bits of the device path's error latch (include/varlen_attn.h, varlen_attn_fwd_device).
 LATCH_BITS = {1: "cu_seqlens_q[0] != 0", 2: "cu_seqlens_q decreases", 4: "cu_seqlens_q[batch] > total_q",
               8: "cu_seqlens_kv[0] != 0", 16: "cu_seqlens_kv decreases", 32: "cu_seqlens_kv[batch] > total_kv",
-              64: "work list overflow"}
+              64: "work list overflow", 128: "cache_seqlens[b] < 0",
+              256: "cache_seqlens[b] + new rows > cache_capacity", 512: "position outside the rotary tables",
+              1024: "kv_seqlens[b] outside [0, cache_capacity]"}
 
 
 def library_path() -> str:
@@ -94,6 +96,12 @@ def load_library():
     lib.varlen_attn_fwd_device.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, i32, f32,
                                            i32, vp, vp, ctypes.c_size_t, vp, vp]
     lib.varlen_attn_fwd_device.restype = ctypes.c_int
+    lib.varlen_attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, f32, i32,
+                                            f32, i32, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.varlen_attn_fwd_kvcache.restype = ctypes.c_int
+    lib.varlen_kv_append_rope.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, i32, i64,
+                                          i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.varlen_kv_append_rope.restype = ctypes.c_int
     lib.varlen_attn_plan.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, i32, f32,
                                      ctypes.POINTER(Options), ctypes.POINTER(PlanStats), vp, i64]
     lib.varlen_attn_plan.restype = ctypes.c_int
@@ -283,6 +291,146 @@ def varlen_attn_fwd_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int,
             cu_seqlens_q.numel() - 1, tq, tkv, hq, hkv, d, dv, code,
             float(scale) if scale else 0.0, 1 if is_causal else 0, float(softcap),
             -1 if local_window is None else int(local_window), out.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), error_latch.data_ptr(), stream)
+    _check(st)
+    return out
+
+
+def _gpu_int32(x, name, n=None):
+    import torch
+    if x is None or not x.is_cuda or x.dtype != torch.int32 or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if n is not None and x.numel() != n:
+        raise ValueError(f"{name} must have {n} elements, got {x.numel()}")
+
+
+def _rows_of(x, width: int, name: str):
+    """Rows and row stride (elements) of a [rows, >= width] view with unit inner stride."""
+    if x.dim() == 3:
+        if x.stride(2) != 1 or x.stride(1) != x.size(2):
+            raise ValueError(f"{name} rows must be dense inside")
+        if x.size(1) * x.size(2) != width:
+            raise ValueError(f"{name} rows must hold {width} elements, got {x.size(1) * x.size(2)}")
+        return x.size(0), x.stride(0)
+    if x.dim() == 2:
+        if x.stride(1) != 1 or x.size(1) != width:
+            raise ValueError(f"{name} must be [rows, {width}] with unit inner stride")
+        return x.size(0), x.stride(0)
+    raise ValueError(f"{name} must be rank 2 or 3")
+
+
+def kv_append_rope(q, k, v, k_cache, v_cache, cu_seqlens_q, cache_seqlens, num_heads: int, kv_num_heads=None,
+                   cos=None, sin=None, position_ids=None, rotary_interleaved: bool = False, q_out=None,
+                   kv_seqlens_out=None, error_latch=None, stream=None):
+    """The step before decode over a fixed-capacity cache: rotary embedding of
+    the new q/k rows and the append of k/v into the caches (one kernel, capture
+    safe). q may be None (no query work); q_out defaults to q (in place).
+    k/v/q may be strided row views (e.g. slices of a packed QKV buffer).
+    Caches are [batch * capacity, Hkv, D] / [..., Dv]. Returns q_out."""
+    import torch
+    lib = load_library()
+    hq = int(num_heads)
+    hkv = int(kv_num_heads) if kv_num_heads else hq
+    if k.dim() != 3 or v.dim() != 3:
+        raise ValueError("k and v must be [rows, kv_heads, head_size] views")
+    d, dv = k.size(2), v.size(2)
+    code = _dtype_code(k)
+    for name, t in (("v", v), ("k_cache", k_cache), ("v_cache", v_cache)) + ((("q", q),) if q is not None else ()):
+        if t.dtype != k.dtype or not t.is_cuda:
+            raise TypeError(f"{name} must be a GPU tensor of the key dtype")
+    tq, ks = _rows_of(k, hkv * d, "k")
+    tv, vs = _rows_of(v, hkv * dv, "v")
+    if tv != tq:
+        raise ValueError("k and v row counts differ")
+    qs = 0
+    if q is not None:
+        tqq, qs = _rows_of(q, hq * d, "q")
+        if tqq != tq:
+            raise ValueError("q and k row counts differ")
+        if q_out is None:
+            q_out = q
+        if not q_out.is_contiguous() or q_out.numel() != tq * hq * d or q_out.dtype != q.dtype:
+            raise ValueError("q_out must be a dense [rows, num_heads, head_size] tensor")
+    for name, t, w in (("k_cache", k_cache, hkv * d), ("v_cache", v_cache, hkv * dv)):
+        if not t.is_contiguous() or t.numel() % w:
+            raise ValueError(f"{name} must be a contiguous [batch * capacity, kv_heads, head_size] tensor")
+    batch = cu_seqlens_q.numel() - 1
+    cap = k_cache.numel() // (hkv * d)
+    if batch < 1 or cap % batch or v_cache.numel() // (hkv * dv) != cap:
+        raise ValueError("cache rows must be batch * capacity for both caches")
+    cap //= batch
+    _gpu_int32(cu_seqlens_q, "cu_seqlens_q")
+    _gpu_int32(cache_seqlens, "cache_seqlens", batch)
+    if kv_seqlens_out is not None:
+        _gpu_int32(kv_seqlens_out, "kv_seqlens_out", batch)
+    if error_latch is None:
+        raise ValueError("error_latch is required")
+    _gpu_int32(error_latch, "error_latch", 1)
+    rdim, rows = 0, 0
+    if cos is not None:
+        if sin is None or cos.shape != sin.shape or cos.dim() != 2:
+            raise ValueError("cos and sin must be equal [rows, rotary_dim / 2] tensors")
+        if cos.dtype != torch.float32 or sin.dtype != torch.float32 or not (cos.is_contiguous() and sin.is_contiguous()):
+            raise TypeError("cos and sin must be contiguous float32 GPU tensors")
+        rows, rdim = cos.size(0), 2 * cos.size(1)
+    if position_ids is not None and (position_ids.dtype != torch.int64 or not position_ids.is_contiguous()
+                                     or position_ids.numel() != tq):
+        raise ValueError("position_ids must be a contiguous int64 tensor with one entry per new row")
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device).cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    with torch.cuda.device(k.device):
+        st = lib.varlen_kv_append_rope(
+            ptr(q), ptr(q_out), k.data_ptr(), v.data_ptr(), qs, ks, vs, k_cache.data_ptr(), v_cache.data_ptr(),
+            cu_seqlens_q.data_ptr(), cache_seqlens.data_ptr(), ptr(kv_seqlens_out), ptr(cos), ptr(sin),
+            ptr(position_ids), batch, tq, hq, hkv, d, dv, code, cap, rdim, rows, 1 if rotary_interleaved else 0,
+            error_latch.data_ptr(), stream)
+    _check(st)
+    return q_out
+
+
+def varlen_attn_fwd_kvcache(q, k_cache, v_cache, cu_seqlens_q, kv_seqlens, num_heads: int, kv_num_heads=None,
+                            scale=None, is_causal: bool = False, softcap: float = 0.0, local_window=None,
+                            out=None, workspace=None, error_latch=None, stream=None):
+    """Capture-safe attention of packed new rows over a fixed-capacity cache
+    ([batch * capacity, Hkv, D]): sequence b reads cache rows
+    [b * capacity, b * capacity + kv_seqlens[b]). Workspace size:
+    device_workspace_bytes(batch, total_q, batch * capacity, ...)."""
+    lib = load_library()
+    hq = int(num_heads)
+    hkv = int(kv_num_heads) if kv_num_heads else hq
+    if not (q.is_cuda and k_cache.is_cuda and v_cache.is_cuda):
+        raise ValueError("q and the caches must be GPU tensors")
+    code = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("Q and the caches must use the same floating dtype")
+    tq, d = _resolve(q, hq, "query")
+    rows, dk = _resolve(k_cache, hkv, "key cache")
+    rows_v, dv = _resolve(v_cache, hkv, "value cache")
+    if dk != d or rows_v != rows:
+        raise ValueError("cache head size / rows do not match")
+    batch = cu_seqlens_q.numel() - 1
+    if batch < 1 or rows % batch:
+        raise ValueError("cache rows must be batch * capacity")
+    _gpu_int32(cu_seqlens_q, "cu_seqlens_q")
+    _gpu_int32(kv_seqlens, "kv_seqlens", batch)
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    if out.dtype != q.dtype or not out.is_contiguous() or out.numel() != tq * hq * dv or not out.is_cuda:
+        raise ValueError("output must be a contiguous GPU tensor of the Q dtype with [total_q, num_heads, v_head_size] elements")
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if error_latch is None:
+        raise ValueError("error_latch is required")
+    _gpu_int32(error_latch, "error_latch", 1)
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib.varlen_attn_fwd_kvcache(
+            q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens_q.data_ptr(), kv_seqlens.data_ptr(),
+            batch, tq, rows // batch, hq, hkv, d, dv, code, float(scale) if scale else 0.0, 1 if is_causal else 0,
+            float(softcap), -1 if local_window is None else int(local_window), out.data_ptr(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), error_latch.data_ptr(), stream)
     _check(st)
     return out

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 RESOURCES_PATH = os.path.join(HERE, "libvarlen_attn.resources.json")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["prefill_mfma.hip", "decode.hip", "prefill_f32.hip", "sched.hip"]
+HIP_SOURCES = ["prefill_mfma.hip", "decode.hip", "prefill_f32.hip", "sched.hip", "rope_append.hip"]
 HOST_SOURCES = ["varlen_attn.cpp"]
 ARCH = "gfx950"
 

@@ -69,6 +69,10 @@ enum LatchBits : int32_t {
   kLatchCuKvOrder = 16,   // cu_seqlens_kv decreases
   kLatchCuKvTotal = 32,   // cu_seqlens_kv[B] > the key/value buffers' rows
   kLatchCapacity = 64,    // a list outgrew its bound (not expected)
+  kLatchPast = 128,       // cache step: a cached length is negative
+  kLatchOverflow = 256,   // cache step: cached + new rows exceed the capacity
+  kLatchPosition = 512,   // cache step: a rotated row's position has no table row
+  kLatchKvLen = 1024,     // attention over a cache: a length is negative or exceeds the capacity
 };
 struct DevicePlan {
   int32_t batch, hq;
@@ -76,11 +80,37 @@ struct DevicePlan {
   int32_t nh_dec, use_decode;               // decode items: nh_dec heads, L_q == 1 sequences
   int32_t causal, window;
   int32_t cap_q, cap_kv;                    // rows of the q/out and k/v buffers
+  // Fixed-capacity cache: non-null kv_len [batch] gives L_kv of each
+  // sequence, whose keys start at row b * kv_capacity; cu_kv is not read.
+  const int32_t* kv_len;
+  int32_t kv_capacity;
   int64_t cap_prefill, cap_decode, cap_combine, cap_partials;
   int32_t* header;
   // [batch + 1] each, used when the batch is too large for the scheduler's LDS
   int32_t *seq_q, *seq_kv, *seq_pre, *seq_decf, *seq_decp, *seq_cmb, *seq_part;
   WorkItem *prefill, *decode, *combine;
+};
+
+// The cache step: rotary embedding of new query/key rows and their append
+// into a fixed-capacity cache (one thread per rotary pair or copied pair).
+struct RopeParams {
+  const void* q;      // [rows, q_stride] new query rows, or null (no query work)
+  void* q_out;        // [total_q, hq, d]; may equal q when q_stride == hq * d
+  const void* k;      // new key rows, k_stride elements apart
+  const void* v;      // new value rows, v_stride elements apart
+  void* k_cache;      // [batch * capacity, hkv, d]
+  void* v_cache;      // [batch * capacity, hkv, dv]
+  const int32_t* cu_q;
+  const int32_t* past;
+  int32_t* kv_len_out;     // [batch] or null
+  const float* cos;        // [rows, rot_half] or null (no rotation)
+  const float* sin;
+  const int64_t* pos_ids;  // [total_q] or null (position past + i)
+  int32_t* latch;
+  int64_t q_stride, k_stride, v_stride;
+  int32_t batch, total_q, hq, hkv, d, dv, capacity, rot_half, rows, interleaved;
+  int32_t units_q, units_k, units_row;  // pair units of one new row (q, then k, then v)
+  int32_t blocks_per_row, row_blocks;   // row workgroups; then the per-sequence workgroups
 };
 
 struct Params {

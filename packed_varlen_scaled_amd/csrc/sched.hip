@@ -25,6 +25,10 @@
 //      workspace);
 //   3. every thread writes items k = tid, tid + 1024, ..., finding the
 //      sequence of item k by binary search over those offsets.
+// With a fixed-capacity KV cache (the attention that follows the cache step)
+// the keys of sequence b are rows [b * capacity, b * capacity + L_kv[b]) and
+// L_kv comes from a device array instead of cu_seqlens_kv; each length is
+// checked against the capacity.
 // The prefill list takes the host scheduler's order: sequences by their
 // longest item (a bitonic sort in LDS; sequence order for batches too large
 // for it), each sequence's row blocks from the last to the first, head
@@ -150,6 +154,11 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
   int32_t* adecp = in_lds ? s_decp : dp.seq_decp;
   int32_t* acmb = in_lds ? s_cmb : dp.seq_cmb;
   int32_t* apart = in_lds ? s_part : dp.seq_part;
+  // Keys of sequence b: packed (akv holds cu_seqlens_kv) or in a
+  // fixed-capacity cache (akv[b] holds L_kv, the keys start at b * capacity).
+  const bool cache = dp.kv_len != nullptr;
+  auto lkv_of = [&](int32_t b) -> int32_t { return cache ? akv[b] : akv[b + 1] - akv[b]; };
+  auto kv0_of = [&](int32_t b) -> int32_t { return cache ? b * dp.kv_capacity : akv[b]; };
 
   // ---- 1. validation (latch first), cu arrays, the decode key total ------------
   const int32_t latched = __hip_atomic_load(latch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -161,22 +170,22 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
   int64_t dec_keys = 0;
   for (int32_t b = tid; b <= B; b += kThreads) {
     aq[b] = cu_q[b];
-    akv[b] = cu_kv[b];
+    akv[b] = cache ? (b < B ? dp.kv_len[b] : 0) : cu_kv[b];
   }
   if (!in_lds) __threadfence();
   __syncthreads();
   if (s_err == 0) {
     if (tid == 0) {
       if (aq[0] != 0) err |= kLatchCuQStart;
-      if (akv[0] != 0) err |= kLatchCuKvStart;
       if (aq[B] > dp.cap_q) err |= kLatchCuQTotal;
-      if (akv[B] > dp.cap_kv) err |= kLatchCuKvTotal;
+      if (!cache && akv[0] != 0) err |= kLatchCuKvStart;
+      if (!cache && akv[B] > dp.cap_kv) err |= kLatchCuKvTotal;
     }
     for (int32_t b = tid; b < B; b += kThreads) {
       const int32_t lq = aq[b + 1] - aq[b];
-      const int32_t lkv = akv[b + 1] - akv[b];
+      const int32_t lkv = lkv_of(b);
       if (lq < 0) err |= kLatchCuQOrder;
-      if (lkv < 0) err |= kLatchCuKvOrder;
+      if (cache ? (lkv < 0 || lkv > dp.kv_capacity) : lkv < 0) err |= cache ? kLatchKvLen : kLatchCuKvOrder;
       if (dp.use_decode && lq == 1 && lkv > 0) dec_keys += lkv;
     }
     if (err) atomicOr(&s_err, err);
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
       if (b < B) {
         int64_t top = 0, last = 0;
         const int32_t lq = aq[b + 1] - aq[b];
-        const int32_t lkv = akv[b + 1] - akv[b];
+        const int32_t lkv = lkv_of(b);
         if (lq > 0 && !(dp.use_decode && lq == 1)) {
           // An item's key range never shrinks from one full row block to the
           // next (causal) or never grows (window without causal), so the
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     Counts n = {0, 0, 0, 0, 0};
     if (b < B) {
       const int32_t lq = aq[b + 1] - aq[b];
-      const int32_t lkv = akv[b + 1] - akv[b];
+      const int32_t lkv = lkv_of(b);
       if (lq > 0) {
         if (dp.use_decode && lq == 1) {
           const DecRange r = dec_range(lq, lkv, dp, dchunk);
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
       const int32_t bd = seq_at2(b);  // short-split counts in their order
       const int32_t lqd = aq[bd + 1] - aq[bd];
       if (dp.use_decode && lqd == 1) {
-        const DecRange r = dec_range(lqd, akv[bd + 1] - akv[bd], dp, dchunk);
+        const DecRange r = dec_range(lqd, lkv_of(bd), dp, dchunk);
         n.decp = g_dec * (r.ns - r.nfull);
       }
     }
@@ -334,9 +343,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     it.partial_base = -1;
     it.n_splits = 1;
     it.q_token0 = aq[b];
-    it.kv_token0 = akv[b];
+    it.kv_token0 = kv0_of(b);
     it.len_q = aq[b + 1] - aq[b];
-    it.len_kv = akv[b + 1] - akv[b];
+    it.len_kv = lkv_of(b);
     it.split = 0;
     it.pad = 0;
     return it;

@@ -29,6 +29,8 @@ hipError_t launch_combine(const Params& p, const WorkItem* items, int n, int dty
 hipError_t launch_prefill_f32(const Params& p, const WorkItem* items, int n, hipStream_t s);
 hipError_t launch_plan(const DevicePlan& dp, const int32_t* cu_q, const int32_t* cu_kv, int32_t* latch,
                        hipStream_t s);
+hipError_t launch_rope_append(const RopeParams& p, int dtype, hipStream_t s);
+int rope_units_per_block();
 }  // namespace pva
 
 namespace {
@@ -36,6 +38,7 @@ namespace {
 using pva::WorkItem;
 
 thread_local std::string g_last_error;
+thread_local const char* g_entry = "varlen_attn_fwd";  // names the failing call in messages
 
 varlen_status_t fail(varlen_status_t code, const char* fmt, ...) {
   char buf[512];
@@ -43,9 +46,16 @@ varlen_status_t fail(varlen_status_t code, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_last_error = std::string("varlen_attn_fwd: ") + buf;
+  g_last_error = std::string(g_entry) + ": " + buf;
   return code;
 }
+
+// Sets the call name of error messages for the duration of an entry point.
+struct EntryName {
+  const char* saved;
+  explicit EntryName(const char* name) : saved(g_entry) { g_entry = name; }
+  ~EntryName() { g_entry = saved; }
+};
 
 // ---------------------------------------------------------------------------
 // Arguments after defaults are resolved.
@@ -697,7 +707,8 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
                            const int32_t* cu_kv_dev, int32_t batch, int64_t total_q, int64_t total_kv,
                            int32_t num_heads, int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
                            int32_t dtype, float scale, int32_t is_causal, float softcap, int32_t local_window,
-                           void* out, void* workspace, size_t workspace_bytes, int32_t* latch, void* stream_v) {
+                           void* out, void* workspace, size_t workspace_bytes, int32_t* latch, void* stream_v,
+                           const int32_t* kv_len_dev = nullptr, int32_t kv_capacity = 0) {
   g_last_error.clear();
   Problem pr;
   varlen_status_t st = check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim,
@@ -706,7 +717,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
   pr.causal = is_causal != 0;
   if ((st = check_window(local_window, &pr)) != VARLEN_OK) return st;
   if ((st = check_supported(pr)) != VARLEN_OK) return st;
-  if (!cu_q_dev || !cu_kv_dev || !latch)
+  if (!cu_q_dev || !(cu_kv_dev || kv_len_dev) || !latch)
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "device cu_seqlens arrays and the error latch must be non-null");
   if (total_q > 0 && (!q || !out))
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "query and output pointers must be non-null");
@@ -736,6 +747,8 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
   dp.window = pr.window;
   dp.cap_q = (int32_t)total_q;
   dp.cap_kv = (int32_t)total_kv;
+  dp.kv_len = kv_len_dev;
+  dp.kv_capacity = kv_capacity;
   dp.cap_prefill = sh.cap_prefill;
   dp.cap_decode = sh.cap_decode;
   dp.cap_combine = sh.cap_combine;
@@ -844,6 +857,113 @@ varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void*
   return run_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv, num_heads, kv_num_heads,
                     head_dim, v_head_dim, dtype, scale, is_causal, softcap, local_window, out, workspace,
                     workspace_bytes, error_latch, stream);
+}
+
+varlen_status_t varlen_attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* cu_seqlens_q, const int32_t* kv_seqlens, int32_t batch,
+                                        int64_t total_q, int32_t cache_capacity, int32_t num_heads,
+                                        int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                                        int32_t dtype, float scale, int32_t is_causal, float softcap,
+                                        int32_t local_window, void* out, void* workspace,
+                                        size_t workspace_bytes, int32_t* error_latch, void* stream) {
+  g_last_error.clear();
+  EntryName name("varlen_attn_fwd_kvcache");
+  if (cache_capacity < 1)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "cache_capacity must be >= 1, got %d", cache_capacity);
+  if (batch >= 1 && (int64_t)batch * cache_capacity > INT32_MAX)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "batch * cache_capacity must stay below 2^31 rows, got %d * %d", batch,
+                cache_capacity);
+  if (!kv_seqlens) return fail(VARLEN_ERR_INVALID_ARGUMENT, "kv_seqlens must be non-null");
+  const int64_t rows = batch >= 1 ? (int64_t)batch * cache_capacity : 0;
+  return run_device(q, k_cache, v_cache, cu_seqlens_q, nullptr, batch, total_q, rows, num_heads, kv_num_heads,
+                    head_dim, v_head_dim, dtype, scale, is_causal, softcap, local_window, out, workspace,
+                    workspace_bytes, error_latch, stream, kv_seqlens, cache_capacity);
+}
+
+varlen_status_t varlen_kv_append_rope(const void* q, void* q_out, const void* k, const void* v,
+                                      int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
+                                      void* k_cache, void* v_cache, const int32_t* cu_seqlens_q,
+                                      const int32_t* cache_seqlens, int32_t* kv_seqlens_out,
+                                      const float* cos_cache, const float* sin_cache,
+                                      const int64_t* position_ids, int32_t batch, int64_t total_q,
+                                      int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                      int32_t v_head_dim, int32_t dtype, int32_t cache_capacity,
+                                      int32_t rotary_dim, int32_t rotary_rows, int32_t rotary_interleaved,
+                                      int32_t* error_latch, void* stream) {
+  g_last_error.clear();
+  EntryName name("varlen_kv_append_rope");
+  Problem pr;
+  varlen_status_t st = check_scalars(batch, total_q, 0, num_heads, kv_num_heads, head_dim, v_head_dim, dtype, 0.f,
+                                     0.f, &pr);
+  if (st != VARLEN_OK) return st;
+  if (pr.d % 2 || pr.dv % 2)
+    return fail(VARLEN_ERR_UNSUPPORTED, "head_dim and v_head_dim must be even, got %d and %d", pr.d, pr.dv);
+  if (cache_capacity < 1)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "cache_capacity must be >= 1, got %d", cache_capacity);
+  if ((int64_t)batch * cache_capacity > INT32_MAX)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "batch * cache_capacity must stay below 2^31 rows, got %d * %d", batch,
+                cache_capacity);
+  if (rotary_dim != 0) {
+    if (rotary_dim < 2 || rotary_dim % 2 || rotary_dim > pr.d)
+      return fail(VARLEN_ERR_INVALID_ARGUMENT, "rotary_dim must be 0 or even in [2, head_dim=%d], got %d", pr.d,
+                  rotary_dim);
+    if (rotary_rows < 1 || !cos_cache || !sin_cache)
+      return fail(VARLEN_ERR_INVALID_ARGUMENT, "rotation needs cos/sin tables with rotary_rows >= 1 rows");
+  }
+  if ((q == nullptr) != (q_out == nullptr))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "q and q_out must both be given or both be null");
+  const int64_t qs = q_row_stride ? q_row_stride : (int64_t)pr.hq * pr.d;
+  const int64_t ks = k_row_stride ? k_row_stride : (int64_t)pr.hkv * pr.d;
+  const int64_t vs = v_row_stride ? v_row_stride : (int64_t)pr.hkv * pr.dv;
+  if (qs < (int64_t)pr.hq * pr.d || ks < (int64_t)pr.hkv * pr.d || vs < (int64_t)pr.hkv * pr.dv)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "row strides must cover a row's heads (q %lld, k %lld, v %lld)",
+                (long long)qs, (long long)ks, (long long)vs);
+  if (q && q_out == q && qs != (int64_t)pr.hq * pr.d)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "in-place rotation (q_out == q) needs dense query rows");
+  if (!k || !v || !k_cache || !v_cache || !cu_seqlens_q || !cache_seqlens || !error_latch)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT,
+                "k, v, the caches, cu_seqlens_q, cache_seqlens and the error latch must be non-null");
+  pva::RopeParams rp;
+  std::memset(&rp, 0, sizeof rp);
+  rp.q = q;
+  rp.q_out = q_out;
+  rp.k = k;
+  rp.v = v;
+  rp.k_cache = k_cache;
+  rp.v_cache = v_cache;
+  rp.cu_q = cu_seqlens_q;
+  rp.past = cache_seqlens;
+  rp.kv_len_out = kv_seqlens_out;
+  rp.cos = rotary_dim ? cos_cache : nullptr;
+  rp.sin = rotary_dim ? sin_cache : nullptr;
+  rp.pos_ids = position_ids;
+  rp.latch = error_latch;
+  rp.q_stride = qs;
+  rp.k_stride = ks;
+  rp.v_stride = vs;
+  rp.batch = batch;
+  rp.total_q = (int32_t)total_q;
+  rp.hq = pr.hq;
+  rp.hkv = pr.hkv;
+  rp.d = pr.d;
+  rp.dv = pr.dv;
+  rp.capacity = cache_capacity;
+  rp.rot_half = rotary_dim / 2;
+  rp.rows = rotary_dim ? rotary_rows : 0;
+  rp.interleaved = rotary_interleaved != 0;
+  rp.units_q = q ? pr.hq * (pr.d / 2) : 0;
+  rp.units_k = pr.hkv * (pr.d / 2);
+  rp.units_row = rp.units_q + rp.units_k + pr.hkv * (pr.dv / 2);
+  const int per_block = pva::rope_units_per_block();
+  rp.blocks_per_row = (rp.units_row + per_block - 1) / per_block;
+  const int64_t row_blocks = total_q * rp.blocks_per_row;
+  if (row_blocks + ((int64_t)batch + 255) / 256 > INT32_MAX)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "too many new rows for one launch");
+  rp.row_blocks = (int32_t)row_blocks;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = timed(6, row_blocks + (batch + 255) / 256, s, [&] { return pva::launch_rope_append(rp, dtype, s); });
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return VARLEN_OK;
 }
 
 varlen_status_t varlen_attn_fwd_ex(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,

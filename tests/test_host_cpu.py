@@ -353,3 +353,60 @@ def test_device_entry_rejects_before_any_device_work(case, fragment):
                                     window, fake, ws, ws_bytes, latch, None)
     msg = lib.varlen_attn_last_error().decode()
     assert st == 1 and fragment in msg, (st, msg)
+
+
+# ---- the cache step and the attention over a cache: host-side validation ------
+def _rope_status(batch=2, total_q=3, hq=4, hkv=2, d=64, dv=0, dtype=2, cap=16, rdim=64, rows=32, inter=0,
+                 q=1, q_out=1, qs=0, ks=0, vs=0, latch=1, cos=1):
+    """varlen_kv_append_rope with dummy (never dereferenced) device pointers:
+    every case here must fail validation before anything is enqueued."""
+    lib = pva.load_library()
+    p = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
+    st = lib.varlen_kv_append_rope(p(q), p(q_out), p(1), p(1), qs, ks, vs, p(1), p(1), p(1), p(1), None,
+                                   p(cos), p(cos), None, batch, total_q, hq, hkv, d, dv, dtype, cap, rdim, rows,
+                                   inter, p(latch), None)
+    return st, lib.varlen_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,fragment", [
+    (dict(d=63), 3, "must be even"),
+    (dict(dv=5), 3, "must be even"),
+    (dict(cap=0), 1, "cache_capacity must be >= 1"),
+    (dict(batch=70000, cap=40000), 1, "below 2^31"),
+    (dict(rdim=3), 1, "rotary_dim must be 0 or even"),
+    (dict(rdim=66), 1, "rotary_dim must be 0 or even"),
+    (dict(rows=0), 1, "rotary_rows >= 1"),
+    (dict(cos=0), 1, "rotary_rows >= 1"),
+    (dict(q_out=0), 1, "q and q_out"),
+    (dict(qs=100), 1, "row strides"),
+    (dict(ks=64), 1, "row strides"),
+    (dict(q=1, q_out=1, qs=300), 1, "in-place rotation"),
+    (dict(latch=0), 1, "must be non-null"),
+    (dict(hq=6, hkv=4), 1, "multiple of kv_num_heads"),
+    (dict(dtype=5), 1, "dtype code"),
+])
+def test_cache_step_rejects_before_any_device_work(kwargs, status, fragment):
+    st, msg = _rope_status(**kwargs)
+    assert st == status, msg
+    assert msg.startswith("varlen_kv_append_rope: ") and fragment in msg, msg
+
+
+def test_cache_attention_rejects_before_any_device_work():
+    lib = pva.load_library()
+    one = ctypes.c_void_p(1)
+
+    def call(cap=16, kvlen=one, batch=2, latch=one):
+        st = lib.varlen_attn_fwd_kvcache(one, one, one, one, kvlen, batch, 3, cap, 4, 2, 64, 0, 2, 0.0, 1, 0.0, -1,
+                                         one, one, 1 << 30, latch, None)
+        return st, lib.varlen_attn_last_error().decode()
+
+    for kw, frag in [(dict(cap=0), "cache_capacity must be >= 1"), (dict(kvlen=None), "kv_seqlens"),
+                     (dict(batch=70000, cap=40000), "below 2^31"), (dict(latch=None), "must be non-null")]:
+        st, msg = call(**kw)
+        assert st == 1 and msg.startswith("varlen_attn_fwd_kvcache: ") and frag in msg, (kw, msg)
+
+
+def test_entry_name_is_restored_after_a_cache_call():
+    _rope_status(cap=0)
+    st, msg = _fwd_status(_cu([3, 4]), _cu([5, 2]), hq=0)
+    assert msg.startswith("varlen_attn_fwd: "), msg
