@@ -9,7 +9,10 @@ validates them and builds the work list, then every attention kernel runs.
 --path device launches the same call eagerly each step; --path host times
 varlen_attn_fwd (host validation and scheduling, work-list upload, kernels).
 The default workload is the ragged causal prefill (B=16, L ~ U{128..2048},
-Hq=32, Hkv=8, D=128, bf16).
+Hq=32, Hkv=8, D=128, bf16). --cache (packed_decode, chunked_prefill_cache)
+times the same attention over a fixed-capacity KV cache instead: a step is
+the cache step (rotary on the new q/k rows, append of k/v into the cache)
+followed by the attention over the cache, both in the graph.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path graph|device|host]
 
@@ -42,7 +45,9 @@ DEFAULT_WORKLOAD = "ragged_causal_prefill"
 KERNEL_SOURCES = {
     "prefill_mfma": ["packed_varlen_scaled_amd/csrc/prefill_mfma.hip", "packed_varlen_scaled_amd/csrc/common.h"],
     "decode": ["packed_varlen_scaled_amd/csrc/decode.hip", "packed_varlen_scaled_amd/csrc/common.h"],
+    "cache_step": ["packed_varlen_scaled_amd/csrc/rope_append.hip", "packed_varlen_scaled_amd/csrc/common.h"],
 }
+CACHE_WORKLOADS = ("packed_decode", "chunked_prefill_cache")
 
 
 def log(*a):
@@ -221,7 +226,13 @@ def main(argv=None) -> int:
                     help="only time a plain library bf16 GEMM (8192^3, torch.matmul -> hipBLASLt) on "
                          "zero, constant and N(0,1) operands, then exit: the MFMA rate the chip sustains "
                          "on data like the workloads', next to the dense spec peak")
+    ap.add_argument("--cache", action="store_true",
+                    help="packed_decode / chunked_prefill_cache over a fixed-capacity KV cache: each step runs "
+                         "the cache step (rotary + append of the new rows) and the attention over the cache")
     a = ap.parse_args(argv)
+    if a.cache and (a.workload not in CACHE_WORKLOADS or a.path == "host" or a.window):
+        print(f"--cache needs one of {CACHE_WORKLOADS}, the device or graph path and no window", file=sys.stderr)
+        return 2
     if a.gemm_ceiling:
         return gemm_ceiling()
     if a.copy_reference:
@@ -291,6 +302,48 @@ def main(argv=None) -> int:
                                    local_window=window or None, out=out, workspace=ws, error_latch=latch)
 
     step = step_host if a.path == "host" else step_device
+    attn_io_bytes = io_bytes  # the attention kernels' own algorithmic bytes
+    cache_bytes = 0
+    if a.cache:
+        # The cache: each sequence's first L_kv - L_q rows are its packed K/V
+        # rows; its last L_q rows are the new rows the cache step appends
+        # (after turning the keys). Slots past L_kv stay unwritten.
+        cap = (max(batch.lkv) + 255) // 256 * 256
+        bsz = len(batch.lq)
+        kc = torch.empty(bsz * cap, w.kv_num_heads, w.head_dim, dtype=batch.k.dtype, device="cuda:0")
+        vc = torch.empty(bsz * cap, w.kv_num_heads, w.dv, dtype=batch.v.dtype, device="cuda:0")
+        new_rows = []
+        past = []
+        for b, (nq, nkv) in enumerate(zip(batch.lq, batch.lkv)):
+            k0 = int(batch.cu_kv[b])
+            kc[b * cap:b * cap + nkv - nq] = batch.k[k0:k0 + nkv - nq]
+            vc[b * cap:b * cap + nkv - nq] = batch.v[k0:k0 + nkv - nq]
+            new_rows.append(torch.arange(k0 + nkv - nq, k0 + nkv, device="cuda:0"))
+            past.append(nkv - nq)
+        idx = torch.cat(new_rows)
+        k_new, v_new = batch.k[idx].contiguous(), batch.v[idx].contiguous()
+        past_t = torch.tensor(past, dtype=torch.int32, device="cuda:0")
+        kv_len_t = torch.empty(bsz, dtype=torch.int32, device="cuda:0")
+        cos, sin = synth.rotary_tables(cap, w.head_dim, device="cuda:0")
+        q_rot = torch.empty_like(batch.q)
+        ws = torch.empty(pva.device_workspace_bytes(bsz, batch.total_q, bsz * cap, w.num_heads, w.kv_num_heads,
+                                                    w.head_dim, w.dv, w.dtype), dtype=torch.uint8, device="cuda:0")
+        el = 4 if w.dtype == "f32" else 2
+        # read q, k, v of the new rows and the two table rows; write q_out and the two cache rows
+        cache_bytes = (2 * batch.total_q * (w.num_heads * w.head_dim + w.kv_num_heads * (w.head_dim + w.dv)) * el
+                       + batch.total_q * w.head_dim * 4)
+        io_bytes += cache_bytes
+        log(f"[bench] cache: capacity {cap} rows/sequence, {kc.numel() * 2 * el / 2**30:.1f} GiB of K+V cache, "
+            f"cache step moves {cache_bytes / 1e6:.1f} MB")
+
+        def step_cache():
+            pva.kv_append_rope(batch.q, k_new, v_new, kc, vc, cu_q, past_t, w.num_heads, w.kv_num_heads, cos=cos,
+                               sin=sin, q_out=q_rot, kv_seqlens_out=kv_len_t, error_latch=latch)
+            pva.varlen_attn_fwd_kvcache(q_rot, kc, vc, cu_q, kv_len_t, w.num_heads, w.kv_num_heads,
+                                        scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap, out=out,
+                                        workspace=ws, error_latch=latch)
+
+        step = step_cache
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -348,7 +401,7 @@ def main(argv=None) -> int:
         kind = "decode"
         k_ms, k_n, _ = prof[kind]
         avg = k_ms / max(k_n, 1)
-        achieved = io_bytes / (avg / 1e3) / 1e9
+        achieved = attn_io_bytes / (avg / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
     else:
@@ -359,11 +412,21 @@ def main(argv=None) -> int:
         achieved = flops / (avg / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS}
-    traffic = load_traffic(kind, a.workload) if kind in KERNEL_SOURCES and not window else None
+    traffic = load_traffic(kind, a.workload) if kind in KERNEL_SOURCES and not window and not a.cache else None
     roof["traffic"] = traffic
     roof["kernel"] = kind
     roof["kernel_avg_ms"] = avg
     roof["launches"] = k_n
+
+    cache_info = None
+    if a.cache:
+        c_ms, c_n, _ = prof["cache_step"]
+        c_avg = c_ms / max(c_n, 1)
+        cache_info = {"kernel_avg_ms": c_avg, "bytes_per_launch": cache_bytes,
+                      "GB/s": cache_bytes / (c_avg / 1e3) / 1e9 if c_avg else None,
+                      "frac_of_hbm_peak": cache_bytes / (c_avg / 1e3) / 1e9 / PEAK_HBM_GBS if c_avg else None,
+                      "capacity_rows": cap}
+        log(f"[bench] cache step {cache_info}")
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -375,8 +438,9 @@ def main(argv=None) -> int:
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": a.workload + (f" + local window {window}" if window else ""),
-                   "local_window": window or None, "call": a.path, "batch": w.batch, "num_heads": w.num_heads,
+        "config": {"workload": a.workload + (f" + local window {window}" if window else "")
+                   + (" over a fixed-capacity KV cache (cache step + attention)" if a.cache else ""),
+                   "local_window": window or None, "call": a.path, "kv_cache": cache_info, "batch": w.batch, "num_heads": w.num_heads,
                    "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,
                    "softcap": w.softcap, "total_q": batch.total_q, "total_kv": batch.total_kv,
                    "valid_pairs": pairs, "flops_per_step": flops, "io_bytes_per_step": io_bytes,

@@ -109,7 +109,9 @@ struct RopeParams {
   int32_t* latch;
   int64_t q_stride, k_stride, v_stride;
   int32_t batch, total_q, hq, hkv, d, dv, capacity, rot_half, rows, interleaved;
-  int32_t units_q, units_k, units_row;  // pair units of one new row (q, then k, then v)
+  int32_t vec;                          // 1: 16-byte pieces; 0: one pair per unit
+  int32_t units_q, units_k, units_row;  // units of one new row (q, then k, then v)
+  int32_t rot_units, head_units_qk, head_units_v;  // 16-byte pieces: turned per q/k head, all per head
   int32_t blocks_per_row, row_blocks;   // row workgroups; then the per-sequence workgroups
 };
 

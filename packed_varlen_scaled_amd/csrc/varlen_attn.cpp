@@ -30,7 +30,7 @@ hipError_t launch_prefill_f32(const Params& p, const WorkItem* items, int n, hip
 hipError_t launch_plan(const DevicePlan& dp, const int32_t* cu_q, const int32_t* cu_kv, int32_t* latch,
                        hipStream_t s);
 hipError_t launch_rope_append(const RopeParams& p, int dtype, hipStream_t s);
-int rope_units_per_block();
+int rope_units_per_block(int vec);
 }  // namespace pva
 
 namespace {
@@ -951,10 +951,29 @@ varlen_status_t varlen_kv_append_rope(const void* q, void* q_out, const void* k,
   rp.rot_half = rotary_dim / 2;
   rp.rows = rotary_dim ? rotary_rows : 0;
   rp.interleaved = rotary_interleaved != 0;
-  rp.units_q = q ? pr.hq * (pr.d / 2) : 0;
-  rp.units_k = pr.hkv * (pr.d / 2);
-  rp.units_row = rp.units_q + rp.units_k + pr.hkv * (pr.dv / 2);
-  const int per_block = pva::rope_units_per_block();
+  // 16-byte pieces when every row, stride and head size is a whole number
+  // of pieces and the rotary dims split into whole pieces (per half for the
+  // half-split pairing); one pair per unit otherwise.
+  const int el = dtype == VARLEN_F32 ? 4 : 2;
+  const int vw = 16 / el;
+  auto aligned16 = [](const void* ptr) { return ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+  const bool vec = pr.d % vw == 0 && pr.dv % vw == 0 && qs % vw == 0 && ks % vw == 0 && vs % vw == 0 &&
+                   (rotary_interleaved ? rotary_dim % vw == 0 : rotary_dim % (2 * vw) == 0) && aligned16(q) &&
+                   aligned16(q_out) && aligned16(k) && aligned16(v) && aligned16(k_cache) && aligned16(v_cache);
+  rp.vec = vec;
+  if (vec) {
+    rp.rot_units = rotary_interleaved ? rotary_dim / vw : rotary_dim / (2 * vw);
+    rp.head_units_qk = rp.rot_units + (pr.d - rotary_dim) / vw;
+    rp.head_units_v = pr.dv / vw;
+    rp.units_q = q ? pr.hq * rp.head_units_qk : 0;
+    rp.units_k = pr.hkv * rp.head_units_qk;
+    rp.units_row = rp.units_q + rp.units_k + pr.hkv * rp.head_units_v;
+  } else {
+    rp.units_q = q ? pr.hq * (pr.d / 2) : 0;
+    rp.units_k = pr.hkv * (pr.d / 2);
+    rp.units_row = rp.units_q + rp.units_k + pr.hkv * (pr.dv / 2);
+  }
+  const int per_block = pva::rope_units_per_block(vec);
   rp.blocks_per_row = (rp.units_row + per_block - 1) / per_block;
   const int64_t row_blocks = total_q * rp.blocks_per_row;
   if (row_blocks + ((int64_t)batch + 255) / 256 > INT32_MAX)

@@ -108,6 +108,12 @@ STEP_CASES = [
     ("bf16_packed_qkv", "bf16", 8, 2, 128, None, [1, 2, 1], [3, 0, 9], 16, 128, True, dict(packed_qkv=True)),
     ("bf16_in_place", "bf16", 8, 2, 64, None, [1, 1, 5], [0, 2, 3], 16, 64, False, dict(in_place=True)),
     ("bf16_fills_capacity", "bf16", 4, 2, 64, None, [3, 1], [13, 15], 16, 64, False, {}),
+    # shapes the 16-byte kernel does not take: one pair per thread
+    ("f32_rotary12_pairs", "f32", 4, 2, 40, None, [2, 1], [3, 0], 16, 12, False, {}),
+    ("bf16_d66_pairs", "bf16", 4, 2, 66, None, [1, 2], [0, 5], 16, 66, False, {}),
+    ("bf16_rotary24_half_pairs", "bf16", 8, 2, 64, None, [1, 3], [4, 9], 16, 24, False, {}),
+    ("bf16_rotary24_interleaved", "bf16", 8, 2, 64, None, [1, 3], [4, 9], 16, 24, True, {}),
+    ("f16_dv72", "f16", 4, 2, 64, 72, [2, 1], [1, 1], 8, 32, False, {}),
 ]
 
 
@@ -365,3 +371,66 @@ def test_decode_step_in_a_graph():
         want = oracle.attention(res["q"].astype(np.float32), kp, vp, step.cu_q, cu_kv, 16, 2, is_causal=True,
                                 dtype="f32").reshape(bsz, 16, 128)
         compare(got.double().cpu().numpy(), want, "bf16")
+
+
+@pytest.mark.parametrize("name", ["packed_decode", "chunked_prefill_cache"])
+def test_full_size_cache_path_sampled(name):
+    """The full-size workload as the benchmark's --cache run launches it: the
+    packed K/V rows fill the cache, the last L_q rows of each sequence are the
+    new rows (turned by the cache step), and sampled sequences are checked
+    against the oracle on the oracle's own rotation of those rows."""
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = synth.WORKLOADS[name]
+    _say("full cache", name)
+    batch = synth.workload_batch(name, device="cuda")
+    bsz = len(batch.lq)
+    cap = (max(batch.lkv) + 255) // 256 * 256
+    kc = torch.empty(bsz * cap, w.kv_num_heads, w.head_dim, dtype=batch.k.dtype, device="cuda")
+    vc = torch.empty(bsz * cap, w.kv_num_heads, w.dv, dtype=batch.v.dtype, device="cuda")
+    idx, past = [], []
+    for b, (nq, nkv) in enumerate(zip(batch.lq, batch.lkv)):
+        k0 = int(batch.cu_kv[b])
+        kc[b * cap:b * cap + nkv - nq] = batch.k[k0:k0 + nkv - nq]
+        vc[b * cap:b * cap + nkv - nq] = batch.v[k0:k0 + nkv - nq]
+        idx.append(torch.arange(k0 + nkv - nq, k0 + nkv, device="cuda"))
+        past.append(nkv - nq)
+    idx = torch.cat(idx)
+    k_new, v_new = batch.k[idx].contiguous(), batch.v[idx].contiguous()
+    cu_q = torch.from_numpy(batch.cu_q).cuda()
+    past_t = torch.tensor(past, dtype=torch.int32, device="cuda")
+    kv_len = torch.empty(bsz, dtype=torch.int32, device="cuda")
+    latch = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cos, sin = synth.rotary_tables(cap, w.head_dim, device="cuda")
+    q_rot = torch.empty_like(batch.q)
+    out = torch.empty(batch.total_q, w.num_heads, w.dv, dtype=batch.q.dtype, device="cuda")
+    ws = torch.empty(pva.device_workspace_bytes(bsz, batch.total_q, bsz * cap, w.num_heads, w.kv_num_heads,
+                                                w.head_dim, w.dv, w.dtype), dtype=torch.uint8, device="cuda")
+    pva.kv_append_rope(batch.q, k_new, v_new, kc, vc, cu_q, past_t, w.num_heads, w.kv_num_heads, cos=cos, sin=sin,
+                       q_out=q_rot, kv_seqlens_out=kv_len, error_latch=latch)
+    pva.varlen_attn_fwd_kvcache(q_rot, kc, vc, cu_q, kv_len, w.num_heads, w.kv_num_heads, scale=w.scale or None,
+                                is_causal=w.is_causal, softcap=w.softcap, out=out, workspace=ws, error_latch=latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0
+    assert kv_len.cpu().tolist() == list(batch.lkv)
+    cs, sn = cos.cpu().numpy().astype(np.float64), sin.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(1)
+    longest = int(np.argmax(np.asarray(batch.lkv)))
+    seqs = sorted({longest, *rng.choice(bsz, size=3, replace=False).tolist()})
+    for b in seqs:
+        q0, q1 = int(batch.cu_q[b]), int(batch.cu_q[b + 1])
+        k0, k1 = int(batch.cu_kv[b]), int(batch.cu_kv[b + 1])
+        nq = q1 - q0
+        qd = _as_f64(batch.q[q0:q1], w.dtype)
+        kd = _as_f64(batch.k[k0:k1], w.dtype)
+        vd = _as_f64(batch.v[k0:k1], w.dtype)
+        pos = past[b] + np.arange(nq)
+        qr = ra.rotate(qd, cs[pos][:, None, :], sn[pos][:, None, :], w.head_dim, False)
+        kd[k1 - k0 - nq:] = ra.rotate(kd[k1 - k0 - nq:], cs[pos][:, None, :], sn[pos][:, None, :], w.head_dim, False)
+        want = oracle.attention(qr.astype(np.float32), kd.astype(np.float32), vd.astype(np.float32), [0, nq],
+                                [0, k1 - k0], w.num_heads, w.kv_num_heads, scale=w.scale or None,
+                                is_causal=w.is_causal, softcap=w.softcap, dtype="f32").reshape(nq, w.num_heads, w.dv)
+        ma, rel = compare(out[q0:q1].double().cpu().numpy(), want, w.dtype)
+        _say("full cache", name, "seq", b, "L_q", nq, "L_kv", k1 - k0, "max_abs", ma, "rel_l2", rel)
+    del batch, kc, vc, out
+    torch.cuda.empty_cache()
