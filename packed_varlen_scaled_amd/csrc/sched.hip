@@ -14,24 +14,27 @@
 // start at 0 and never decrease), with the packed totals read as buffer
 // capacities: cu[B] may not exceed them.
 //
-// One workgroup of 1024 threads:
+// One workgroup of 1024 threads, written for few barriers (each costs a few
+// hundred cycles with 16 waves):
 //   1. every thread validates and counts the items of its sequences; the
 //      split-KV chunk needs the total decode key count, so that is reduced
 //      first;
-//   2. one exclusive scan over the sequences (five counts at once) gives each
-//      sequence's first item in the prefill list, in the two parts of the
-//      decode list, in the combine list, and its first partial row; the
-//      offsets and the cu arrays stay in LDS when the batch fits (else in the
-//      workspace);
-//   3. every thread writes items k = tid, tid + 1024, ..., finding the
-//      sequence of item k by binary search over those offsets.
+//   2. the sequence orders (a rank sort: every sequence counts the sequences
+//      that go before it) and one exclusive scan over the sequences (five
+//      counts at once, wave prefix sums then one pass over the wave totals)
+//      give each sequence's first item in the prefill list, in the two parts
+//      of the decode list, in the combine list, and its first partial row;
+//      the offsets and the cu arrays stay in LDS when the batch fits (else in
+//      the workspace, without sorting);
+//   3. each wave writes 64 consecutive items at a time, finding the sequence
+//      of item k by binary search over those offsets; the items pass through
+//      LDS so that the wave's stores cover whole 64-byte items back to back.
 // With a fixed-capacity KV cache (the attention that follows the cache step)
 // the keys of sequence b are rows [b * capacity, b * capacity + L_kv[b]) and
 // L_kv comes from a device array instead of cu_seqlens_kv; each length is
 // checked against the capacity.
 // The prefill list takes the host scheduler's order: sequences by their
-// longest item (a bitonic sort in LDS; sequence order for batches too large
-// for it), each sequence's row blocks from the last to the first, head
+// longest item, each sequence's row blocks from the last to the first, head
 // groups innermost. The decode list holds every full-chunk split first and
 // the shorter last splits after them, longest first, so that the last items
 // handed to the GPU are the short ones.
@@ -42,6 +45,7 @@ namespace pva {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
 constexpr int kLdsSeq = 2048;  // batches of up to kLdsSeq - 1 keep their offsets in LDS
 
 __device__ int32_t visible_end_dev(int32_t lq, int32_t lkv, int32_t r0, int32_t rows, int32_t causal) {
@@ -60,26 +64,36 @@ struct Counts {
   int32_t pre, decf, decp, cmb, part;
 };
 
-// Exclusive scan of one Counts per thread over the workgroup; *total gets the sums.
-__device__ Counts block_exclusive_scan(Counts v, Counts* buf, Counts* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    Counts add = {0, 0, 0, 0, 0};
-    if (tid >= off) add = buf[tid - off];
-    __syncthreads();
-    buf[tid].pre += add.pre;
-    buf[tid].decf += add.decf;
-    buf[tid].decp += add.decp;
-    buf[tid].cmb += add.cmb;
-    buf[tid].part += add.part;
-    __syncthreads();
+__device__ Counts add(Counts a, Counts b) {
+  return Counts{a.pre + b.pre, a.decf + b.decf, a.decp + b.decp, a.cmb + b.cmb, a.part + b.part};
+}
+
+// Exclusive scan of one Counts per thread over the workgroup; *total gets
+// the sums. Wave prefix sums by lane shifts, then every thread adds the
+// totals of the waves before its own: two barriers.
+__device__ Counts block_exclusive_scan(Counts v, Counts* wave_tot, Counts* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  Counts incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const Counts o = {__shfl_up(incl.pre, off, 64), __shfl_up(incl.decf, off, 64), __shfl_up(incl.decp, off, 64),
+                      __shfl_up(incl.cmb, off, 64), __shfl_up(incl.part, off, 64)};
+    if (lane >= off) incl = add(incl, o);
   }
-  const Counts incl = buf[tid];
-  *total = buf[kThreads - 1];
+  if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  return Counts{incl.pre - v.pre, incl.decf - v.decf, incl.decp - v.decp, incl.cmb - v.cmb, incl.part - v.part};
+  Counts before = {0, 0, 0, 0, 0}, all = {0, 0, 0, 0, 0};
+#pragma unroll 2
+  for (int w = 0; w < kWaves; ++w) {
+    const Counts t = wave_tot[w];
+    if (w < wave) before = add(before, t);
+    all = add(all, t);
+  }
+  __syncthreads();  // wave_tot is reused by the next scan
+  *total = all;
+  return Counts{before.pre + incl.pre - v.pre, before.decf + incl.decf - v.decf, before.decp + incl.decp - v.decp,
+                before.cmb + incl.cmb - v.cmb, before.part + incl.part - v.part};
 }
 
 // Largest b in [0, n) with off[b] <= k (off is non-decreasing, off[0] == 0).
@@ -92,26 +106,22 @@ __device__ int32_t owner(const int32_t* off, int32_t n, int32_t k) {
   return lo;
 }
 
-// Sorts key[0, n) in descending order (n a power of two <= kLdsSeq), the
-// whole workgroup taking part.
-__device__ void bitonic_sort_desc(int64_t* key, int32_t n) {
-  const int tid = threadIdx.x;
-  for (int32_t k = 2; k <= n; k <<= 1) {
-    for (int32_t j = k >> 1; j > 0; j >>= 1) {
-      for (int32_t i = tid; i < n; i += kThreads) {
-        const int32_t ixj = i ^ j;
-        if (ixj > i) {
-          const int64_t a = key[i], c = key[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (a < c) : (a > c)) {
-            key[i] = c;
-            key[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
+// Writes the items of lanes with k0 + lane < n at list[k0 + lane]; every
+// lane of the wave calls it together. Each lane's 64-byte item goes to LDS,
+// then the wave stores the 64 items as consecutive 16-byte pieces.
+__device__ void store_items(WorkItem* list, int32_t k0, int32_t n, const WorkItem& it, u32x4_t* stage) {
+  const int lane = threadIdx.x & 63;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(&it);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) stage[lane * 4 + c] = src[c];
+  __builtin_amdgcn_wave_barrier();
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(list + k0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int c = lane + 64 * r;  // piece c holds quarter c % 4 of item c / 4
+    if (k0 + c / 4 < n) dst[c] = stage[c];
   }
+  __builtin_amdgcn_wave_barrier();
 }
 
 // The split-KV key range of the single row of a decode sequence.
@@ -128,32 +138,39 @@ __device__ DecRange dec_range(int32_t lq, int32_t lkv, const DevicePlan& dp, int
   return r;
 }
 
-}  // namespace
+struct SchedLds {
+  int32_t q[kLdsSeq], kv[kLdsSeq];                    // cu arrays (cache: kv holds L_kv)
+  int32_t pre[kLdsSeq], decf[kLdsSeq], decp[kLdsSeq];  // list offsets
+  int32_t cmb[kLdsSeq], part[kLdsSeq];
+  int32_t ord[kLdsSeq], ord2[kLdsSeq];  // position -> sequence: prefill order, short-split order
+  union {
+    struct {
+      int64_t cost[kLdsSeq], cost2[kLdsSeq];  // sort keys
+    } sort;
+    u32x4_t stage[kWaves][256];  // item staging, 4 KB per wave
+  } u;
+  Counts wave_tot[kWaves];
+  int32_t err, has_pre, has_dec;
+  int64_t dec_keys;
+};
 
-__global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int32_t* __restrict__ cu_q,
-                                                        const int32_t* __restrict__ cu_kv, int32_t* latch) {
-  __shared__ Counts scan_buf[kThreads];
-  __shared__ int32_t s_q[kLdsSeq], s_kv[kLdsSeq];                    // cu arrays
-  __shared__ int32_t s_pre[kLdsSeq], s_decf[kLdsSeq], s_decp[kLdsSeq];  // list offsets
-  __shared__ int32_t s_cmb[kLdsSeq], s_part[kLdsSeq];
-  __shared__ int64_t s_key[kLdsSeq];   // prefill order of the sequences (LDS path)
-  __shared__ int64_t s_key2[kLdsSeq];  // order of the sequences' short last decode splits
-  __shared__ int32_t s_err;
-  __shared__ int32_t s_dchunk;
-  __shared__ int64_t s_dec_keys;
+// The scheduler; LDS selects where the per-sequence arrays live (LDS, or the
+// workspace for batches too large for it).
+template <bool LDS>
+__device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
+                          int32_t* latch, SchedLds& sh) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int32_t B = dp.batch;
   int32_t* header = dp.header;
-  const bool in_lds = B + 1 <= kLdsSeq;
-  // offsets and cu values live in LDS or (large batches) in the workspace;
-  // generic pointers read either
-  int32_t* aq = in_lds ? s_q : dp.seq_q;
-  int32_t* akv = in_lds ? s_kv : dp.seq_kv;
-  int32_t* apre = in_lds ? s_pre : dp.seq_pre;
-  int32_t* adecf = in_lds ? s_decf : dp.seq_decf;
-  int32_t* adecp = in_lds ? s_decp : dp.seq_decp;
-  int32_t* acmb = in_lds ? s_cmb : dp.seq_cmb;
-  int32_t* apart = in_lds ? s_part : dp.seq_part;
+  int32_t* aq = LDS ? sh.q : dp.seq_q;
+  int32_t* akv = LDS ? sh.kv : dp.seq_kv;
+  int32_t* apre = LDS ? sh.pre : dp.seq_pre;
+  int32_t* adecf = LDS ? sh.decf : dp.seq_decf;
+  int32_t* adecp = LDS ? sh.decp : dp.seq_decp;
+  int32_t* acmb = LDS ? sh.cmb : dp.seq_cmb;
+  int32_t* apart = LDS ? sh.part : dp.seq_part;
   // Keys of sequence b: packed (akv holds cu_seqlens_kv) or in a
   // fixed-capacity cache (akv[b] holds L_kv, the keys start at b * capacity).
   const bool cache = dp.kv_len != nullptr;
@@ -163,18 +180,20 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
   // ---- 1. validation (latch first), cu arrays, the decode key total ------------
   const int32_t latched = __hip_atomic_load(latch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (tid == 0) {
-    s_err = latched != 0 ? -1 : 0;
-    s_dec_keys = 0;
+    sh.err = latched != 0 ? -1 : 0;
+    sh.dec_keys = 0;
+    sh.has_pre = 0;
+    sh.has_dec = 0;
   }
-  int32_t err = 0;
-  int64_t dec_keys = 0;
   for (int32_t b = tid; b <= B; b += kThreads) {
     aq[b] = cu_q[b];
     akv[b] = cache ? (b < B ? dp.kv_len[b] : 0) : cu_kv[b];
   }
-  if (!in_lds) __threadfence();
+  if (!LDS) __threadfence();
   __syncthreads();
-  if (s_err == 0) {
+  if (sh.err == 0) {
+    int32_t err = 0, has_pre = 0, has_dec = 0;
+    int64_t dec_keys = 0;
     if (tid == 0) {
       if (aq[0] != 0) err |= kLatchCuQStart;
       if (aq[B] > dp.cap_q) err |= kLatchCuQTotal;
@@ -186,15 +205,20 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
       const int32_t lkv = lkv_of(b);
       if (lq < 0) err |= kLatchCuQOrder;
       if (cache ? (lkv < 0 || lkv > dp.kv_capacity) : lkv < 0) err |= cache ? kLatchKvLen : kLatchCuKvOrder;
-      if (dp.use_decode && lq == 1 && lkv > 0) dec_keys += lkv;
+      const bool dec = dp.use_decode && lq == 1;
+      if (dec && lkv > 0) dec_keys += lkv;
+      has_dec |= dec;
+      has_pre |= lq > 0 && !dec;
     }
-    if (err) atomicOr(&s_err, err);
-    if (dec_keys) atomicAdd((unsigned long long*)&s_dec_keys, (unsigned long long)dec_keys);
+    if (err) atomicOr(&sh.err, err);
+    if (dec_keys) atomicAdd((unsigned long long*)&sh.dec_keys, (unsigned long long)dec_keys);
+    if (has_pre) sh.has_pre = 1;
+    if (has_dec) sh.has_dec = 1;
   }
   __syncthreads();
-  if (s_err != 0) {
+  if (sh.err != 0) {
     if (tid == 0) {
-      if (s_err > 0) atomicOr(latch, s_err);
+      if (sh.err > 0) atomicOr(latch, sh.err);
       header[kHdrPrefill] = 0;
       header[kHdrDecode] = 0;
       header[kHdrCombine] = 0;
@@ -204,69 +228,85 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     return;
   }
   // split-KV chunk: the host scheduler's rule (enough items to fill the chip
-  // several times, 512..8192 keys, a multiple of 128)
-  if (tid == 0) {
+  // several times, 512..8192 keys, a multiple of 128); every thread works it
+  // out from the shared total
+  int32_t dchunk;
+  {
     const int64_t groups = dp.hq / dp.nh_dec;
-    int64_t c = (s_dec_keys * groups + 2047) / 2048;
+    int64_t c = (sh.dec_keys * groups + 2047) / 2048;
     c = max((int64_t)512, min((int64_t)8192, c));
-    s_dchunk = (int32_t)((c + 127) / 128 * 128);
+    dchunk = (int32_t)((c + 127) / 128 * 128);
   }
-  __syncthreads();
-  const int32_t dchunk = s_dchunk;
   const int32_t g_pre = dp.hq / dp.nh;      // head groups of a prefill item
   const int32_t g_dec = dp.hq / dp.nh_dec;  // head groups of a decode item
+  const bool need_pre = sh.has_pre != 0;
+  const bool need_dec = sh.has_dec != 0;
 
-  // ---- 2a. sequence orders (LDS path; sequence order for batches too large for
-  // it). Prefill: by the cost of the sequence's longest item, descending, ties
-  // by index (the host scheduler's order). Short last decode splits: by length,
-  // descending. key = value << 11 | (2047 - b).
-  const bool sorted = in_lds;
-  if (sorted) {
-    int32_t n = 1;
-    while (n < B) n <<= 1;
-    for (int32_t b = tid; b < n; b += kThreads) {
-      int64_t key = -1, key2 = -1;
-      if (b < B) {
-        int64_t top = 0, last = 0;
-        const int32_t lq = aq[b + 1] - aq[b];
-        const int32_t lkv = lkv_of(b);
-        if (lq > 0 && !(dp.use_decode && lq == 1)) {
-          // An item's key range never shrinks from one full row block to the
-          // next (causal) or never grows (window without causal), so the
-          // longest item is in the first, the second-to-last or the last
-          // (possibly short) row block.
-          const int32_t n_rb = (lq + dp.rows_per_item - 1) / dp.rows_per_item;
-          const int32_t cand[3] = {0, max(0, n_rb - 2), n_rb - 1};
-          for (int32_t ci = 0; ci < 3; ++ci) {
-            const int32_t rb = cand[ci];
-            const int32_t r0 = rb * dp.rows_per_item;
-            const int32_t rows = min(dp.rows_per_item, lq - r0);
-            const int32_t vb = visible_begin_dev(lq, lkv, r0, dp.window);
-            const int32_t ve = max(vb, visible_end_dev(lq, lkv, r0, rows, dp.causal));
-            top = max(top, (int64_t)(ve - vb) * rows);
-          }
-        } else if (lq == 1) {
-          const DecRange r = dec_range(lq, lkv, dp, dchunk);
-          last = (r.ve - r.vb) - (int64_t)r.nfull * dchunk;  // keys of the short last split
+  // ---- 2a. sequence orders (LDS path). Prefill: by the cost of the sequence's
+  // longest item, descending, ties by index (the host scheduler's order).
+  // Short last decode splits: by length, descending, ties by index.
+  if (LDS) {
+    for (int32_t b = tid; b < B; b += kThreads) {
+      int64_t top = 0, last = 0;
+      const int32_t lq = aq[b + 1] - aq[b];
+      const int32_t lkv = lkv_of(b);
+      if (lq > 0 && !(dp.use_decode && lq == 1)) {
+        // An item's key range never shrinks from one full row block to the
+        // next (causal) or never grows (window without causal), so the
+        // longest item is in the first, the second-to-last or the last
+        // (possibly short) row block.
+        const int32_t n_rb = (lq + dp.rows_per_item - 1) / dp.rows_per_item;
+        const int32_t cand[3] = {0, max(0, n_rb - 2), n_rb - 1};
+        for (int32_t ci = 0; ci < 3; ++ci) {
+          const int32_t rb = cand[ci];
+          const int32_t r0 = rb * dp.rows_per_item;
+          const int32_t rows = min(dp.rows_per_item, lq - r0);
+          const int32_t vb = visible_begin_dev(lq, lkv, r0, dp.window);
+          const int32_t ve = max(vb, visible_end_dev(lq, lkv, r0, rows, dp.causal));
+          top = max(top, (int64_t)(ve - vb) * rows);
         }
-        key = (top << 11) | (int64_t)(kLdsSeq - 1 - b);
-        key2 = (last << 11) | (int64_t)(kLdsSeq - 1 - b);
+      } else if (lq == 1) {
+        const DecRange r = dec_range(lq, lkv, dp, dchunk);
+        last = (r.ve - r.vb) - (int64_t)r.nfull * dchunk;  // keys of the short last split
       }
-      s_key[b] = key;
-      s_key2[b] = key2;
+      sh.u.sort.cost[b] = top;
+      sh.u.sort.cost2[b] = last;
     }
     __syncthreads();
-    bitonic_sort_desc(s_key, n);
-    bitonic_sort_desc(s_key2, n);
+    // rank of sequence b: the sequences with a larger key, or an equal key
+    // and a smaller index. tpk threads (neighbouring lanes) share a key and
+    // count every tpk-th other key, so all 16 waves take part for small
+    // batches; their counts are summed across the lanes.
+    int32_t tpk = 1;
+    while (tpk < 64 && tpk * 2 * B <= kThreads) tpk *= 2;
+    const int32_t part = tid & (tpk - 1);
+    for (int32_t b0 = 0; b0 < B; b0 += kThreads / tpk) {
+      const int32_t b = b0 + tid / tpk;
+      int32_t r = 0, r2 = 0;
+      if (b < B) {
+        const int64_t mine = sh.u.sort.cost[b], mine2 = sh.u.sort.cost2[b];
+#pragma unroll 8
+        for (int32_t j = part; j < B; j += tpk) {
+          const int64_t c = sh.u.sort.cost[j], c2 = sh.u.sort.cost2[j];
+          r += (c > mine) | ((c == mine) & (j < b));
+          r2 += (c2 > mine2) | ((c2 == mine2) & (j < b));
+        }
+      }
+      for (int32_t m = 1; m < tpk; m <<= 1) {
+        r += __shfl_xor(r, m, 64);
+        r2 += __shfl_xor(r2, m, 64);
+      }
+      if (b < B && part == 0) {
+        if (need_pre) sh.ord[r] = b;
+        if (need_dec) sh.ord2[r2] = b;
+      }
+    }
+    __syncthreads();
   }
   // the sequence at position p of the prefill list order / of the decode
   // list's short-split order
-  auto seq_at = [&](int32_t pos) -> int32_t {
-    return sorted ? (int32_t)(kLdsSeq - 1 - (s_key[pos] & (kLdsSeq - 1))) : pos;
-  };
-  auto seq_at2 = [&](int32_t pos) -> int32_t {
-    return sorted ? (int32_t)(kLdsSeq - 1 - (s_key2[pos] & (kLdsSeq - 1))) : pos;
-  };
+  auto seq_at = [&](int32_t pos) -> int32_t { return LDS && need_pre ? sh.ord[pos] : pos; };
+  auto seq_at2 = [&](int32_t pos) -> int32_t { return LDS && need_dec ? sh.ord2[pos] : pos; };
 
   // ---- 2b. per-sequence counts, one scan of all five ------------------------------
   // (prefill counts are taken in prefill order, the others in sequence order)
@@ -276,29 +316,31 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     Counts n = {0, 0, 0, 0, 0};
     if (b < B) {
       const int32_t lq = aq[b + 1] - aq[b];
-      const int32_t lkv = lkv_of(b);
-      if (lq > 0) {
-        if (dp.use_decode && lq == 1) {
-          const DecRange r = dec_range(lq, lkv, dp, dchunk);
-          n.decf = g_dec * r.nfull;
-          if (r.ns > 1) {
-            n.cmb = g_dec;
-            n.part = g_dec * r.ns * dp.nh_dec;
-          }
+      if (dp.use_decode && lq == 1) {
+        const DecRange r = dec_range(lq, lkv_of(b), dp, dchunk);
+        n.decf = g_dec * r.nfull;
+        if (r.ns > 1) {
+          n.cmb = g_dec;
+          n.part = g_dec * r.ns * dp.nh_dec;
         }
       }
-      const int32_t bp = seq_at(b);  // prefill counts in prefill order
-      const int32_t lqp = aq[bp + 1] - aq[bp];
-      if (lqp > 0 && !(dp.use_decode && lqp == 1)) n.pre = ((lqp + dp.rows_per_item - 1) / dp.rows_per_item) * g_pre;
-      const int32_t bd = seq_at2(b);  // short-split counts in their order
-      const int32_t lqd = aq[bd + 1] - aq[bd];
-      if (dp.use_decode && lqd == 1) {
-        const DecRange r = dec_range(lqd, lkv_of(bd), dp, dchunk);
-        n.decp = g_dec * (r.ns - r.nfull);
+      if (need_pre) {
+        const int32_t bp = seq_at(b);  // prefill counts in prefill order
+        const int32_t lqp = aq[bp + 1] - aq[bp];
+        if (lqp > 0 && !(dp.use_decode && lqp == 1))
+          n.pre = ((lqp + dp.rows_per_item - 1) / dp.rows_per_item) * g_pre;
+      }
+      if (need_dec) {
+        const int32_t bd = seq_at2(b);  // short-split counts in their order
+        const int32_t lqd = aq[bd + 1] - aq[bd];
+        if (dp.use_decode && lqd == 1) {
+          const DecRange r = dec_range(lqd, lkv_of(bd), dp, dchunk);
+          n.decp = g_dec * (r.ns - r.nfull);
+        }
       }
     }
     Counts tot;
-    const Counts o = block_exclusive_scan(n, scan_buf, &tot);
+    const Counts o = block_exclusive_scan(n, sh.wave_tot, &tot);
     if (b <= B) {
       apre[b] = base.pre + o.pre;
       adecf[b] = base.decf + o.decf;
@@ -306,11 +348,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
       acmb[b] = base.cmb + o.cmb;
       apart[b] = base.part + o.part;
     }
-    base.pre += tot.pre;
-    base.decf += tot.decf;
-    base.decp += tot.decp;
-    base.cmb += tot.cmb;
-    base.part += tot.part;
+    base = add(base, tot);
   }
   const int64_t n_dec = (int64_t)base.decf + base.decp;
   // the lists must fit their bounds (they size the launch grids)
@@ -326,10 +364,11 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     }
     return;
   }
-  if (!in_lds) __threadfence();
+  if (!LDS) __threadfence();
   __syncthreads();
 
-  // ---- 3. the items ---------------------------------------------------------------
+  // ---- 3. the items, 64 per wave at a time ------------------------------------------
+  u32x4_t* stage = sh.u.stage[wave];
   auto proto = [&](int32_t b, int32_t kind) {
     WorkItem it;
     it.kind = kind;
@@ -350,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     it.pad = 0;
     return it;
   };
-  for (int32_t k = tid; k < base.pre; k += kThreads) {
+  auto make_pre = [&](int32_t k) {
     const int32_t pos = owner(apre, B, k);
     const int32_t b = seq_at(pos);
     const int32_t j = k - apre[pos];
@@ -363,9 +402,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     it.heads = dp.nh;
     it.kv_begin = visible_begin_dev(it.len_q, it.len_kv, it.q_row_begin, dp.window);
     it.kv_end = max(it.kv_begin, visible_end_dev(it.len_q, it.len_kv, it.q_row_begin, it.q_rows, dp.causal));
-    dp.prefill[k] = it;
-  }
-  for (int32_t k = tid; k < n_dec; k += kThreads) {
+    return it;
+  };
+  auto make_dec = [&](int32_t k) {
     const bool full = k < base.decf;
     const int32_t* off = full ? adecf : adecp;
     const int32_t kk = full ? k : k - base.decf;
@@ -389,9 +428,9 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
       it.kv_begin = r.vb + s * dchunk;
       it.kv_end = min(r.ve, r.vb + (s + 1) * dchunk);
     }
-    dp.decode[k] = it;
-  }
-  for (int32_t k = tid; k < base.cmb; k += kThreads) {
+    return it;
+  };
+  auto make_cmb = [&](int32_t k) {
     const int32_t b = owner(acmb, B, k);
     const int32_t gi = k - acmb[b];
     WorkItem it = proto(b, kCombine);
@@ -403,8 +442,22 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
     it.n_splits = r.ns;
     it.kv_begin = r.vb;
     it.kv_end = r.ve;
-    dp.combine[k] = it;
-  }
+    return it;
+  };
+  // Two 64-item chunks per wave and pass, so that the lookups of one hide
+  // under those of the other.
+  auto emit = [&](WorkItem* list, int32_t n, auto make) {
+    for (int32_t k0 = wave * 64; k0 < n; k0 += 2 * kThreads) {
+      const int32_t k1 = k0 + kThreads;
+      const WorkItem a = make(min(k0 + lane, n - 1));
+      const WorkItem c = make(min(k1 + lane, n - 1));
+      store_items(list, k0, n, a, stage);
+      if (k1 < n) store_items(list, k1, n, c, stage);
+    }
+  };
+  emit(dp.prefill, base.pre, make_pre);
+  emit(dp.decode, (int32_t)n_dec, make_dec);
+  emit(dp.combine, base.cmb, make_cmb);
   if (tid == 0) {
     header[kHdrPrefill] = base.pre;
     header[kHdrDecode] = (int32_t)n_dec;
@@ -414,9 +467,21 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
   }
 }
 
+}  // namespace
+
+template <bool LDS>
+__global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int32_t* __restrict__ cu_q,
+                                                        const int32_t* __restrict__ cu_kv, int32_t* latch) {
+  __shared__ SchedLds sh;
+  plan_body<LDS>(dp, cu_q, cu_kv, latch, sh);
+}
+
 hipError_t launch_plan(const DevicePlan& dp, const int32_t* cu_q, const int32_t* cu_kv, int32_t* latch,
                        hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kThreads), 0, s, dp, cu_q, cu_kv, latch);
+  if (dp.batch + 1 <= kLdsSeq)
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kThreads), 0, s, dp, cu_q, cu_kv, latch);
+  else
+    hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kThreads), 0, s, dp, cu_q, cu_kv, latch);
   return hipGetLastError();
 }
 

@@ -439,16 +439,24 @@ DeviceShape device_shape(const Problem& pr) {
     d.nh_dec = largest_pow2_divisor_upto(pr.group, 16);
     d.use_decode = 1;
   }
-  // every sequence adds at most one partial row block
-  d.cap_prefill = ((pr.total_q + d.rows_per_item - 1) / d.rows_per_item + B) * (pr.hq / d.nh);
+  // These bounds size the launch grids (workgroups past the device-built
+  // count return at once), so they are kept tight. Prefill: every prefill
+  // sequence adds at most one partial row block, and with the decode path a
+  // prefill sequence has at least two rows.
+  const int64_t n_pre_seq = std::min<int64_t>(B, d.use_decode ? pr.total_q / 2 : pr.total_q);
+  d.cap_prefill = ((pr.total_q + d.rows_per_item - 1) / d.rows_per_item + n_pre_seq) * (pr.hq / d.nh);
   if (d.use_decode) {
-    // The split-KV chunk is at least ceil(decode keys * groups / 2048) unless
-    // clamped to 8192, so a group splits into at most
-    // max(2048 / groups, total_kv / 8192) + 1 + B items.
+    // A decode sequence has one row, so there are at most min(B, total_q).
+    // The split-KV chunk c is at least 512 and at least ceil(decode keys *
+    // groups / 2048) unless clamped to 8192, so the splits of one head group
+    // number at most decode keys / c + (decode sequences) with decode keys / c
+    // <= min(total_kv / 512, max(2048 / groups, total_kv / 8192)).
     const int64_t g = pr.hq / d.nh_dec;
-    const int64_t per = std::max<int64_t>((2048 + g - 1) / g, (pr.total_kv + 8191) / 8192) + 1 + B;
-    d.cap_decode = g * per;
-    d.cap_combine = g * B;
+    const int64_t n_dec_seq = std::min<int64_t>(B, pr.total_q);
+    const int64_t per_chunk = std::min<int64_t>((pr.total_kv + 511) / 512,
+                                                std::max<int64_t>((2048 + g - 1) / g, (pr.total_kv + 8191) / 8192));
+    d.cap_decode = g * (per_chunk + 1 + n_dec_seq);
+    d.cap_combine = g * n_dec_seq;
     d.cap_partials = d.cap_decode * d.nh_dec;
   }
   size_t off = 0;
@@ -480,6 +488,9 @@ struct DeviceState {
   hipEvent_t copied = nullptr;  // after the last work-list upload
   hipEvent_t done = nullptr;    // after the last call's kernels
   bool pending = false;
+  // device path: decode + combine run on `side` beside prefill (fork/join)
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 constexpr int kMaxDevices = 64;
@@ -792,8 +803,72 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
     p.tanh_log2 = 2.f * pr.scale / pr.softcap * log2e;
   }
 
+  // A decode-dominated batch (no more query rows than sequences) runs
+  // decode + combine on a side stream beside the (at most small) prefill
+  // launch: a fork after the scheduler, a join before the call returns. The
+  // decode kernel then starts right after the scheduler (measured: +2.4 % on
+  // the packed decode workload). Other batches keep one stream: there the
+  // early-exit workgroups of an empty decode launch running beside prefill
+  // would take dispatch slots from the prefill grid and shift its XCD-aware
+  // item order (measured: -2 % on the prefill workloads). The side stream
+  // and its two events are made once per device, outside any graph capture.
+  std::unique_lock<std::mutex> side_lock;
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  if (sh.cap_prefill > 0 && sh.cap_decode > 0 && total_q <= batch) {
+    int dev_id = 0;
+    PVA_HIP(hipGetDevice(&dev_id), "hipGetDevice");
+    if (dev_id >= 0 && dev_id < kMaxDevices) {
+      DeviceState& ds = g_dev[dev_id];
+      side_lock = std::unique_lock<std::mutex>(ds.mu);
+      if (!ds.side) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+          hipStream_t st = nullptr;
+          hipEvent_t f = nullptr, j = nullptr;
+          if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess &&
+              hipEventCreateWithFlags(&f, hipEventDisableTiming) == hipSuccess &&
+              hipEventCreateWithFlags(&j, hipEventDisableTiming) == hipSuccess) {
+            ds.side = st;
+            ds.fork = f;
+            ds.join = j;
+          } else {  // no side stream: the kernels run one after another
+            if (f) (void)hipEventDestroy(f);
+            if (j) (void)hipEventDestroy(j);
+            if (st) (void)hipStreamDestroy(st);
+          }
+        }
+      }
+      side = ds.side;
+      fork_ev = ds.fork;
+      join_ev = ds.join;
+    }
+  }
+
   hipError_t e = timed(5, 1, stream, [&] { return pva::launch_plan(dp, cu_q_dev, cu_kv_dev, latch, stream); });
   pva::Params pp = p;
+  auto launch_decode_combine = [&](hipStream_t s) {
+    hipError_t ee = hipSuccess;
+    if (sh.cap_decode > 0) {
+      pva::Params pd = p;
+      pd.item_count = dp.header + pva::kHdrDecode;
+      ee = timed(2, sh.cap_decode, s,
+                 [&] { return pva::launch_decode(pd, dp.decode, (int)sh.cap_decode, pr.dtype, s); });
+    }
+    if (ee == hipSuccess && sh.cap_combine > 0) {
+      pva::Params pc = p;
+      pc.item_count = dp.header + pva::kHdrCombine;
+      ee = timed(3, sh.cap_combine, s,
+                 [&] { return pva::launch_combine(pc, dp.combine, (int)sh.cap_combine, pr.dtype, s); });
+    }
+    return ee;
+  };
+  if (e == hipSuccess && side) {
+    e = hipEventRecord(fork_ev, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork_ev, 0);
+    if (e == hipSuccess) e = launch_decode_combine(side);
+    if (e == hipSuccess) e = hipEventRecord(join_ev, side);
+  }
   if (e == hipSuccess && sh.cap_prefill > 0) {
     pp.item_count = dp.header + pva::kHdrPrefill;
     if (pr.dtype == VARLEN_F32) {
@@ -805,16 +880,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
       });
     }
   }
-  if (e == hipSuccess && sh.cap_decode > 0) {
-    pp.item_count = dp.header + pva::kHdrDecode;
-    e = timed(2, sh.cap_decode, stream,
-              [&] { return pva::launch_decode(pp, dp.decode, (int)sh.cap_decode, pr.dtype, stream); });
-  }
-  if (e == hipSuccess && sh.cap_combine > 0) {
-    pp.item_count = dp.header + pva::kHdrCombine;
-    e = timed(3, sh.cap_combine, stream,
-              [&] { return pva::launch_combine(pp, dp.combine, (int)sh.cap_combine, pr.dtype, stream); });
-  }
+  if (e == hipSuccess) e = side ? hipStreamWaitEvent(stream, join_ev, 0) : launch_decode_combine(stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return VARLEN_OK;
 }
@@ -1077,16 +1143,24 @@ varlen_status_t varlen_attn_release(void) {
   for (int d = 0; d < kMaxDevices; ++d) {
     DeviceState& ds = g_dev[d];
     std::lock_guard<std::mutex> lock(ds.mu);
-    if (!ds.dev && !ds.host && !ds.copied) continue;
+    if (!ds.dev && !ds.host && !ds.copied && !ds.side) continue;
     if (d < n) (void)hipSetDevice(d);
     if (ds.done) (void)hipEventSynchronize(ds.done);
     if (ds.dev) (void)hipFree(ds.dev);
     if (ds.host) (void)hipHostFree(ds.host);
     if (ds.copied) (void)hipEventDestroy(ds.copied);
     if (ds.done) (void)hipEventDestroy(ds.done);
+    if (ds.side) {
+      (void)hipStreamSynchronize(ds.side);
+      (void)hipStreamDestroy(ds.side);
+    }
+    if (ds.fork) (void)hipEventDestroy(ds.fork);
+    if (ds.join) (void)hipEventDestroy(ds.join);
     ds.dev = ds.host = nullptr;
     ds.dev_cap = ds.host_cap = 0;
     ds.copied = ds.done = nullptr;
+    ds.side = nullptr;
+    ds.fork = ds.join = nullptr;
     ds.pending = false;
   }
   if (n > 0) (void)hipSetDevice(cur);

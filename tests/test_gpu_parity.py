@@ -394,6 +394,8 @@ DEVICE = [
     ("bf16_d128_dv64", dict(hq=8, hkv=2, dv=64), [1, 100, 1, 257], [3000, 700, 129, 300], None),
     ("f16_d64_dv128_window", dict(dtype="f16", hq=8, hkv=2, d=64, dv=128), [40, 1, 100], [300, 2000, 100], 48),
     ("f32_gqa", dict(dtype="f32", hq=8, hkv=2, d=64), [70, 1, 33], [70, 200, 40], None),
+    # no more rows than sequences: decode + combine run on a side stream
+    ("bf16_decode_dominated_mixed", dict(hq=16, hkv=2), [1, 2, 1, 0, 1, 0], [900, 3, 5000, 7, 1, 300], None),
 ]
 
 
@@ -503,6 +505,63 @@ def test_graph_capture_replays_with_new_lengths():
         assert int(latch.item()) == 0
         assert torch.equal(out[:bt.total_q], want), rep
         assert bool((out[bt.total_q:] == 5.0).all()), rep  # rows past cu_seqlens_q[-1] untouched
+
+
+def test_graph_capture_decode_dominated_batch():
+    """The side-stream form (a batch with no more rows than sequences: decode
+    + combine beside prefill) captured once and replayed with new lengths,
+    including prefill rows; every replay equals the eager host-planned call."""
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = _workload(hq=16, hkv=2)
+    B, cap_q, cap_kv = 6, 6, 9000
+    q = torch.zeros(cap_q, 16, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(cap_kv, 2, 128, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(cap_kv, 2, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(cap_q, 16, 128, dtype=torch.bfloat16, device="cuda")
+    cu_q = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    cu_kv = torch.zeros(B + 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(pva.device_workspace_bytes(B, cap_q, cap_kv, 16, 2, 128), dtype=torch.uint8, device="cuda")
+    latch = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def load(bt):
+        q.zero_(), k.zero_(), v.zero_()
+        q[:bt.total_q].copy_(bt.q)
+        k[:bt.total_kv].copy_(bt.k)
+        v[:bt.total_kv].copy_(bt.v)
+        cu_q.copy_(torch.from_numpy(bt.cu_q))
+        cu_kv.copy_(torch.from_numpy(bt.cu_kv))
+
+    def call():
+        pva.varlen_attn_fwd_device(q, k, v, cu_q, cu_kv, 16, 2, is_causal=True, out=out, workspace=ws,
+                                   error_latch=latch)
+
+    shapes = [([1, 1, 1, 1, 1, 1], [3000, 20, 1, 900, 2500, 7]), ([1, 2, 1, 0, 1, 0], [900, 3, 5000, 7, 1, 300]),
+              ([3, 0, 1, 1, 0, 1], [3, 0, 4000, 2, 0, 1000]), ([1, 1, 0, 1, 1, 1], [1, 1, 0, 6000, 100, 1800])]
+    load(_batch(w, *shapes[0]))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the graph (creates the side stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    _say("capturing decode-dominated")
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep, (lq, lkv) in enumerate(shapes):
+        bt = _batch(_workload(hq=16, hkv=2, seed=60 + rep), lq, lkv)
+        want = run_gpu(bt).clone()
+        load(bt)
+        out.fill_(5.0)
+        torch.cuda.synchronize()
+        _say("replay", rep, lq, lkv)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(latch.item()) == 0
+        assert torch.equal(out[:bt.total_q], want), rep
+        assert bool((out[bt.total_q:] == 5.0).all()), rep
 
 
 def test_device_scheduler_large_batch():

@@ -410,3 +410,64 @@ def test_entry_name_is_restored_after_a_cache_call():
     _rope_status(cap=0)
     st, msg = _fwd_status(_cu([3, 4]), _cu([5, 2]), hq=0)
     assert msg.startswith("varlen_attn_fwd: "), msg
+
+
+def _device_caps(batch, total_q, total_kv, hq, hkv, f32=False):
+    """The launch-grid bounds the device path sizes its lists with."""
+    group = hq // hkv
+
+    def pow2_div(g, cap):
+        p = 1
+        while p * 2 <= cap and g % (p * 2) == 0:
+            p *= 2
+        return p
+    if f32:
+        nh, rows, use_dec, nh_dec = 1, 32, False, 1
+    else:
+        nh = pow2_div(group, 8)
+        rows = 32 * (1 if nh >= 4 else 4 // nh)
+        use_dec, nh_dec = True, pow2_div(group, 16)
+    n_pre_seq = min(batch, total_q // 2 if use_dec else total_q)
+    cap_pre = (-(-total_q // rows) + n_pre_seq) * (hq // nh)
+    if not use_dec:
+        return cap_pre, 0, 0, 0, nh, rows
+    g = hq // nh_dec
+    n_dec_seq = min(batch, total_q)
+    per_chunk = min(-(-total_kv // 512), max(-(-2048 // g), -(-total_kv // 8192)))
+    cap_dec = g * (per_chunk + 1 + n_dec_seq)
+    return cap_pre, cap_dec, g * n_dec_seq, cap_dec * nh_dec, nh, rows
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_device_list_bounds_hold(seed):
+    """The device path's list bounds size its launch grids; a list that
+    outgrew one would latch an error, so they must hold for every batch. The
+    host scheduler emits the same decode items (same chunk rule) and the
+    prefill items are counted directly."""
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        b = int(rng.integers(1, 300))
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        hq = hkv * int(rng.choice([1, 2, 4, 8, 16]))
+        kind = rng.integers(0, 4)
+        if kind == 0:    # all decode, short and empty caches
+            lq = np.ones(b, dtype=np.int64)
+            lkv = rng.integers(0, 40, size=b)
+        elif kind == 1:  # all decode, long caches
+            lq = np.ones(b, dtype=np.int64)
+            lkv = rng.integers(1, 70000, size=b)
+        elif kind == 2:  # mixed
+            lq = rng.choice([1, 1, 1, 2, 7, 300], size=b)
+            lkv = lq + rng.integers(0, 5000, size=b)
+        else:            # prefill
+            lq = rng.integers(0, 900, size=b)
+            lkv = lq + rng.integers(0, 50, size=b)
+        cq, ckv = _cu(lq), _cu(lkv)
+        tq, tkv = int(cq[-1]), int(ckv[-1])
+        cap_pre, cap_dec, cap_cmb, cap_part, nh, rows = _device_caps(b, tq, tkv, hq, hkv)
+        stats, _ = pva.plan(cq, ckv, hq, hkv, head_dim=128, dtype="bf16", is_causal=True)
+        n_pre = sum(-(-int(x) // rows) for x in lq if x >= 2) * (hq // nh)
+        assert n_pre <= cap_pre, (b, hq, hkv, n_pre, cap_pre)
+        assert stats["n_decode_items"] <= cap_dec, (b, hq, hkv, kind, stats, cap_dec)
+        assert stats["n_combine_items"] <= cap_cmb, (stats, cap_cmb)
+        assert stats["n_partials"] <= cap_part, (stats, cap_part)
