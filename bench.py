@@ -425,7 +425,7 @@ def main(argv=None) -> int:
         cache_info = {"kernel_avg_ms": c_avg, "bytes_per_launch": cache_bytes,
                       "GB/s": cache_bytes / (c_avg / 1e3) / 1e9 if c_avg else None,
                       "frac_of_hbm_peak": cache_bytes / (c_avg / 1e3) / 1e9 / PEAK_HBM_GBS if c_avg else None,
-                      "capacity_rows": cap}
+                      "traffic": load_traffic("cache_step", a.workload), "capacity_rows": cap}
         log(f"[bench] cache step {cache_info}")
 
     cpu = None
