@@ -240,13 +240,29 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
 
     // ---- mask and tile max ---------------------------------------------------
     if constexpr (MASK) {
+      // Register r of sacc[mt] holds key kt + 4*half + c with the constant
+      // c = 32*mt + 8*(r/4) + r%4, so each key test is one compare of a
+      // constant against a per-lane bound (two with a window).
+      const int base = kt + 4 * half;
+      const int hi = key_hi - base;
+      if (p.window > 0) {
+        const int lo = key_lo - base;
 #pragma unroll
-      for (int mt = 0; mt < BN / 32; ++mt) {
+        for (int mt = 0; mt < BN / 32; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool bad = key > key_hi || key < key_lo;
-          sacc[mt][r] = bad ? ninf() : sacc[mt][r];
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * mt + 8 * (r >> 2) + (r & 3);
+            sacc[mt][r] = (c > hi || c < lo) ? ninf() : sacc[mt][r];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < BN / 32; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = 32 * mt + 8 * (r >> 2) + (r & 3);
+            sacc[mt][r] = c > hi ? ninf() : sacc[mt][r];
+          }
         }
       }
     }
