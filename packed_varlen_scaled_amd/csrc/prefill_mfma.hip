@@ -86,8 +86,11 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   using VS = TileShape<DV, NW>;
 
   // K0 K1 V0 V1, each [key][d] with 16-byte chunk c of row r stored at chunk
-  // c ^ chunk_perm<row width>(r).
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * KS::TILE + 2 * VS::TILE];
+  // c ^ chunk_perm<row width>(r). After the key loop the same bytes stage
+  // each wave's 32 x DV output tile (OST elements per wave).
+  constexpr int OST = 32 * DV;
+  constexpr int LDS_ELEMS = (2 * KS::TILE + 2 * VS::TILE) > NW * OST ? (2 * KS::TILE + 2 * VS::TILE) : NW * OST;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   constexpr int V0 = 2 * KS::TILE;  // first V buffer
 
   if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
@@ -442,26 +445,49 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       m_ref = ninf();
       l_run = 0.f;
       run_pass(std::true_type{});
+      __syncthreads();  // every wave is done with the key tiles before the output reuses the LDS
     }
   }
 
-  if (!wave_active || !row_ok) return;
   // oacc[mb][r] is the output of row l32 at head dim 32*mb + 8*(r/4) + 4*half + r%4.
   const float l_tot = sum_with_partner32(l_run);
   const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
   if (it.partial_base < 0) {
-    uint16_t* dst = static_cast<uint16_t*>(p.out) + (tok * p.hq + head) * DV;
+    // Each lane holds pieces of one row, so direct stores would write 16
+    // bytes into each of 32 rows per instruction. Instead every wave stages
+    // its normalised tile in its own LDS region ([row][DV], 16-byte chunk c
+    // of row r at c ^ (r % CPR)) and stores whole rows: lane i writes chunk
+    // i % CPR of row 64/CPR * k + i / CPR. The barrier of the overflow check
+    // above has passed, so no wave reads the key tiles any more.
+    constexpr int CPR = DV / 8;         // 16-byte chunks per output row
+    constexpr int RPS = 64 / CPR;       // rows per store instruction
+    uint16_t* ost = lds + wave * OST;
+    if (wave_active) {
 #pragma unroll
-    for (int mb = 0; mb < DV / 32; ++mb) {
+      for (int mb = 0; mb < DV / 32; ++mb) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = 32 * mb + 8 * u + 4 * half;
-        const u32x2_t w = {pack2<BF16>(oacc[mb][4 * u] * inv, oacc[mb][4 * u + 1] * inv),
-                           pack2<BF16>(oacc[mb][4 * u + 2] * inv, oacc[mb][4 * u + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(dst + d) = w;
+        for (int u = 0; u < 4; ++u) {
+          const int c = 4 * mb + u;  // chunk of head dims 32*mb + 8*u .. +7
+          const u32x2_t w = {pack2<BF16>(oacc[mb][4 * u] * inv, oacc[mb][4 * u + 1] * inv),
+                             pack2<BF16>(oacc[mb][4 * u + 2] * inv, oacc[mb][4 * u + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(ost + l32 * DV + ((c ^ (l32 % CPR)) << 3) + 4 * half) = w;
+        }
+      }
+    }
+    __syncthreads();
+    if (!wave_active) return;
+    const int c = lane % CPR;
+#pragma unroll
+    for (int k = 0; k < 32 / RPS; ++k) {
+      const int r = k * RPS + lane / CPR;
+      if (row0 + r < it.q_rows) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(ost + r * DV + ((c ^ (r % CPR)) << 3));
+        const int64_t t = (int64_t)it.q_token0 + it.q_row_begin + row0 + r;
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) + (t * p.hq + head) * DV + 8 * c) = w;
       }
     }
   } else {
+    if (!wave_active || !row_ok) return;
     const int64_t pidx = partial_index(it, it.split, my_row, hh);
     float* po = p.part_o + pidx * DV;
 #pragma unroll

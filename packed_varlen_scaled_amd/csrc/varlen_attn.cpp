@@ -152,6 +152,15 @@ varlen_status_t check_cu(const int32_t* cu, int32_t batch, int64_t total, const 
   return VARLEN_OK;
 }
 
+// The bf16/f16 kernels move q, k, v and out in 16-byte pieces.
+varlen_status_t check_aligned(const Problem& pr, const void* q, const void* k, const void* v, const void* out) {
+  if (pr.dtype == VARLEN_F32) return VARLEN_OK;
+  auto a16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(out))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "f16/bf16 q, k, v and out must be 16-byte aligned");
+  return VARLEN_OK;
+}
+
 varlen_status_t check_supported(const Problem& pr) {
   if (pr.dtype == VARLEN_F32) {
     if (pr.d > 128 || pr.dv > 128)
@@ -603,6 +612,7 @@ varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* 
   pr.cu_q = cu_q_host;
   pr.cu_kv = cu_kv_host;
   if (total_q == 0) return VARLEN_OK;
+  if ((st = check_aligned(pr, q, k, v, out)) != VARLEN_OK) return st;
 
   Plan plan;
   if ((st = build_plan(pr, resolve_options(options), plan)) != VARLEN_OK) return st;
@@ -734,6 +744,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "query and output pointers must be non-null");
   if (total_kv > 0 && (!k || !v))
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "key and value pointers must be non-null");
+  if ((st = check_aligned(pr, q, k, v, out)) != VARLEN_OK) return st;
   const DeviceShape sh = device_shape(pr);
   if (!workspace || workspace_bytes < sh.total)
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "workspace holds %zu bytes, the call needs %zu (varlen_attn_device_workspace_bytes)",

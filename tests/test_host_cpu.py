@@ -81,6 +81,7 @@ def _fwd_status(cu_q, cu_kv, hq=4, hkv=2, d=64, dv=0, dtype=2, scale=0.0, causal
     (dict(d=32, dv=64), 3, "f16/bf16 support head_dim"),
     (dict(dtype=0, d=256), 3, "f32 supports"),
     (dict(ptr=0), 1, "must be non-null"),
+    (dict(ptr=8), 1, "16-byte aligned"),
 ])
 def test_validation_rejects_before_any_device_work(kwargs, status, fragment):
     st, msg = _fwd_status(_cu([3, 4]), _cu([5, 2]), **kwargs)
@@ -333,6 +334,7 @@ def test_device_workspace_size():
     ("misaligned", "256-byte aligned"),
     ("bad_window", "local_window"),
     ("bad_heads", "multiple of kv_num_heads"),
+    ("misaligned_out", "16-byte aligned"),
 ])
 def test_device_entry_rejects_before_any_device_work(case, fragment):
     lib = pva.load_library()
@@ -349,8 +351,9 @@ def test_device_entry_rejects_before_any_device_work(case, fragment):
         window = -3
     elif case == "bad_heads":
         hkv = 3
+    out = ctypes.c_void_p((1 << 20) + 8) if case == "misaligned_out" else fake
     st = lib.varlen_attn_fwd_device(fake, fake, fake, fake, fake, 2, 64, 64, 8, hkv, 128, 0, 2, 0.0, 1, 0.0,
-                                    window, fake, ws, ws_bytes, latch, None)
+                                    window, out, ws, ws_bytes, latch, None)
     msg = lib.varlen_attn_last_error().decode()
     assert st == 1 and fragment in msg, (st, msg)
 
