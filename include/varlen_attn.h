@@ -104,7 +104,11 @@ typedef enum {
  *
  * GPU kernels exist for: bf16 and f16 with head_dim and v_head_dim each in
  * {64, 128} (the two may differ); f32 with head_dim, v_head_dim <= 128.
- * Anything else returns VARLEN_ERR_UNSUPPORTED.
+ * Anything else returns VARLEN_ERR_UNSUPPORTED. With bf16 and f16, q, k, v
+ * and out must be 16-byte aligned (the kernels move 16-byte pieces);
+ * otherwise the call returns VARLEN_ERR_INVALID_ARGUMENT, after the other
+ * checks and before any launch (a call with total_q == 0 is not checked).
+ * varlen_attn_fwd_device and varlen_attn_fwd_kvcache apply the same rule.
  *
  * Buffers q, k, v, the cu arrays and out are borrowed and must stay valid
  * until the enqueued work completes. The library keeps a grow-only
