@@ -29,8 +29,14 @@
 
 namespace pva {
 
+// One wave per SIMD for the 128-dim kernels: fewer loads in flight per CU
+// streamed faster (measured +1.5 % on the packed decode batch).
+template <int D, int DV>
+constexpr int decode_waves_per_eu() { return (D == 128 && DV == 128) ? 1 : 4; }
+
 template <int D, int DV, bool BF16, bool SOFTCAP>
-__global__ __launch_bounds__(256) void decode_kernel(Params p, const WorkItem* __restrict__ items) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, decode_waves_per_eu<D, DV>())))
+void decode_kernel(Params p, const WorkItem* __restrict__ items) {
   constexpr int NW = 4;
   constexpr int BK = 32;            // keys per wave step
   constexpr int VSD = BK + 4;       // per-wave LDS V^T row stride (16-bit elements)
