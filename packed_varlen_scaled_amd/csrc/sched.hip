@@ -14,8 +14,12 @@
 // start at 0 and never decrease), with the packed totals read as buffer
 // capacities: cu[B] may not exceed them.
 //
-// One workgroup of 1024 threads, written for few barriers (each costs a few
-// hundred cycles with 16 waves):
+// Workgroups of 1024 threads, written for few barriers (each costs a few
+// hundred cycles with 16 waves). When the per-sequence arrays fit in LDS,
+// eight workgroups each run steps 1 and 2 on their own copy and write every
+// eighth group of item chunks in step 3 (the first one also writes the
+// header and the latch); a larger batch keeps its arrays in the workspace
+// and runs in one workgroup:
 //   1. every thread validates and counts the items of its sequences; the
 //      split-KV chunk needs the total decode key count, so that is reduced
 //      first;
@@ -47,6 +51,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLdsSeq = 2048;  // batches of up to kLdsSeq - 1 keep their offsets in LDS
+constexpr int kPlanGroups = 8;  // workgroups of the LDS path (the workspace path uses one)
 
 __device__ int32_t visible_end_dev(int32_t lq, int32_t lkv, int32_t r0, int32_t rows, int32_t causal) {
   if (!causal) return lkv;
@@ -163,6 +168,10 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int32_t B = dp.batch;
+  // With several workgroups (LDS path only) every one of them works out the
+  // same per-sequence offsets in its own LDS and writes its share of the
+  // items; only the first writes the header and the latch.
+  const bool lead = blockIdx.x == 0;
   int32_t* header = dp.header;
   int32_t* aq = LDS ? sh.q : dp.seq_q;
   int32_t* akv = LDS ? sh.kv : dp.seq_kv;
@@ -217,7 +226,7 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
   }
   __syncthreads();
   if (sh.err != 0) {
-    if (tid == 0) {
+    if (tid == 0 && lead) {
       if (sh.err > 0) atomicOr(latch, sh.err);
       header[kHdrPrefill] = 0;
       header[kHdrDecode] = 0;
@@ -354,7 +363,7 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
   // the lists must fit their bounds (they size the launch grids)
   if (base.pre > dp.cap_prefill || n_dec > dp.cap_decode || base.cmb > dp.cap_combine ||
       base.part > dp.cap_partials) {
-    if (tid == 0) {
+    if (tid == 0 && lead) {
       atomicOr(latch, kLatchCapacity);
       header[kHdrPrefill] = 0;
       header[kHdrDecode] = 0;
@@ -445,10 +454,11 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
     return it;
   };
   // Two 64-item chunks per wave and pass, so that the lookups of one hide
-  // under those of the other.
+  // under those of the other; the workgroups take interleaved chunks.
+  const int32_t span = kThreads * (int32_t)gridDim.x;  // items of one chunk per wave of every workgroup
   auto emit = [&](WorkItem* list, int32_t n, auto make) {
-    for (int32_t k0 = wave * 64; k0 < n; k0 += 2 * kThreads) {
-      const int32_t k1 = k0 + kThreads;
+    for (int32_t k0 = ((int32_t)blockIdx.x * kWaves + wave) * 64; k0 < n; k0 += 2 * span) {
+      const int32_t k1 = k0 + span;
       const WorkItem a = make(min(k0 + lane, n - 1));
       const WorkItem c = make(min(k1 + lane, n - 1));
       store_items(list, k0, n, a, stage);
@@ -458,7 +468,7 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
   emit(dp.prefill, base.pre, make_pre);
   emit(dp.decode, (int32_t)n_dec, make_dec);
   emit(dp.combine, base.cmb, make_cmb);
-  if (tid == 0) {
+  if (tid == 0 && lead) {
     header[kHdrPrefill] = base.pre;
     header[kHdrDecode] = (int32_t)n_dec;
     header[kHdrCombine] = base.cmb;
@@ -479,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void plan_kernel(DevicePlan dp, const int
 hipError_t launch_plan(const DevicePlan& dp, const int32_t* cu_q, const int32_t* cu_kv, int32_t* latch,
                        hipStream_t s) {
   if (dp.batch + 1 <= kLdsSeq)
-    hipLaunchKernelGGL(plan_kernel<true>, dim3(1), dim3(kThreads), 0, s, dp, cu_q, cu_kv, latch);
+    hipLaunchKernelGGL(plan_kernel<true>, dim3(kPlanGroups), dim3(kThreads), 0, s, dp, cu_q, cu_kv, latch);
   else
     hipLaunchKernelGGL(plan_kernel<false>, dim3(1), dim3(kThreads), 0, s, dp, cu_q, cu_kv, latch);
   return hipGetLastError();
