@@ -204,6 +204,28 @@ def gemm_ceiling() -> int:
     return 0
 
 
+def read_ceiling(gib: float) -> int:
+    """Streaming-read rate of device memory (the reference for the decode
+    kernel's HBM rate): runs the read_ceiling program that the build makes,
+    as a child process, before this process touches the GPU."""
+    import subprocess
+    exe = os.path.join(ROOT, "packed_varlen_scaled_amd", "read_ceiling")
+    if not os.path.exists(exe):
+        print(f"{exe} is not built; run python -m packed_varlen_scaled_amd.build", file=sys.stderr)
+        return 1
+    res = subprocess.run([exe, str(gib)], capture_output=True, text=True)
+    for line in res.stdout.splitlines():
+        log(f"[read] {line}")
+    if res.returncode != 0:
+        print(res.stderr, file=sys.stderr)
+        return res.returncode
+    best = json.loads(res.stdout.strip().splitlines()[-1])
+    best["peak"] = PEAK_HBM_GBS
+    best["frac_of_peak"] = best["read_ceiling_GB/s"] / PEAK_HBM_GBS
+    print(json.dumps(best), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +248,9 @@ def main(argv=None) -> int:
                     help="only time a plain library bf16 GEMM (8192^3, torch.matmul -> hipBLASLt) on "
                          "zero, constant and N(0,1) operands, then exit: the MFMA rate the chip sustains "
                          "on data like the workloads', next to the dense spec peak")
+    ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="GIB",
+                    help="only run the streaming-read program over a GIB-gibibyte buffer (grid and loads in "
+                         "flight swept), then exit: the read rate device memory sustains, next to the HBM spec")
     ap.add_argument("--cache", action="store_true",
                     help="packed_decode / chunked_prefill_cache over a fixed-capacity KV cache: each step runs "
                          "the cache step (rotary + append of the new rows) and the attention over the cache")
@@ -235,6 +260,8 @@ def main(argv=None) -> int:
         return 2
     if a.gemm_ceiling:
         return gemm_ceiling()
+    if a.read_ceiling:
+        return read_ceiling(a.read_ceiling)
     if a.copy_reference:
         import torch
         n = a.copy_reference << 20
