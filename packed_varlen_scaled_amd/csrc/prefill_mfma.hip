@@ -36,8 +36,11 @@
 //     the score layout leaves the keys in), V^T fragments gathered from the
 //     [key][d] tile with the LDS transpose read; the row sum l is taken from
 //     the same rounded P (v_dot2), so numerator and denominator agree.
-// Rows of the tile that lie past the sequence are never stored; keys at or
-// past kv_end are zero-filled in LDS (so data of the next sequence can never
+// The normalised output goes through LDS (each wave's 32 x DV tile, in the
+// bytes the key tiles used) so that the stores cover whole rows, and is
+// written with the nontemporal hint: it is never read again here. Rows of
+// the tile that lie past the sequence are never stored; keys at or past
+// kv_end are zero-filled in LDS (so data of the next sequence can never
 // reach a product) and masked.
 #include <climits>
 #include <type_traits>
@@ -483,7 +486,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       if (row0 + r < it.q_rows) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(ost + r * DV + ((c ^ (r % CPR)) << 3));
         const int64_t t = (int64_t)it.q_token0 + it.q_row_begin + row0 + r;
-        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) + (t * p.hq + head) * DV + 8 * c) = w;
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.out) + (t * p.hq + head) * DV + 8 * c));
       }
     }
   } else {
