@@ -231,6 +231,9 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="after the --warmup steps, keep running untimed steps until this many seconds have "
+                         "passed (clocks settle under load); the JSON's warmup field counts every warm-up step")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -371,10 +374,23 @@ def main(argv=None) -> int:
                                         workspace=ws, error_latch=latch)
 
         step = step_cache
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
+    def warm_up(fn):
+        # W untimed steps, then more until warmup_seconds have passed: the
+        # GPU's clocks take a while to settle under load (the first
+        # milliseconds run at lower clocks), and the timed steps should see
+        # the steady state
+        n, t0 = 0, time.perf_counter()
+        while n < a.warmup or time.perf_counter() - t0 < a.warmup_seconds:
+            fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return n
+
+    warm_steps = warm_up(step)
     graph = None
+    graph_warm = 0
     if a.path == "graph":
         # kernel times come from eagerly launched device-path steps (a graph
         # replay records no events); the timed steps below are replays
@@ -394,10 +410,8 @@ def main(argv=None) -> int:
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-        for _ in range(a.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-    log(f"[bench] warmup {a.warmup} done; timing {a.steps} steps ({a.path} path)")
+        graph_warm = warm_up(graph.replay)
+    log(f"[bench] warmup {warm_steps} steps (+{graph_warm} graph replays) done; timing {a.steps} steps ({a.path} path)")
     if graph is None:
         pva.profile_enable(True)
     torch.cuda.synchronize()
@@ -462,12 +476,13 @@ def main(argv=None) -> int:
         log(f"[bench] cpu_baseline {cpu}")
 
     line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": warm_steps,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": a.workload + (f" + local window {window}" if window else "")
                    + (" over a fixed-capacity KV cache (cache step + attention)" if a.cache else ""),
-                   "local_window": window or None, "call": a.path, "kv_cache": cache_info, "batch": w.batch, "num_heads": w.num_heads,
+                   "local_window": window or None, "call": a.path, "warmup_seconds": a.warmup_seconds,
+                   "graph_warmup_replays": graph_warm, "kv_cache": cache_info, "batch": w.batch, "num_heads": w.num_heads,
                    "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,
                    "softcap": w.softcap, "total_q": batch.total_q, "total_kv": batch.total_kv,
                    "valid_pairs": pairs, "flops_per_step": flops, "io_bytes_per_step": io_bytes,
