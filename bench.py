@@ -166,7 +166,7 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0, window: int = 0):
                       f"{reps} pass(es), {dt * reps:.1f} s"}
 
 
-def gemm_ceiling() -> int:
+def gemm_ceiling(warmup_seconds: float = 1.0) -> int:
     """bf16 GEMM throughput by operand data. MFMA throughput on this chip
     depends on the operand bits (the clock drops as more bits toggle), so the
     dense spec peak is reached only on near-constant data."""
@@ -185,8 +185,14 @@ def gemm_ceiling() -> int:
         else:
             a = torch.randn(n, n, dtype=torch.float32, device="cuda:0", generator=g).to(torch.bfloat16)
             b = torch.randn(n, n, dtype=torch.float32, device="cuda:0", generator=g).to(torch.bfloat16)
-        for _ in range(3):
+        # at least 3 products, then more until warmup_seconds have passed (the
+        # clocks settle under load, as for the attention steps)
+        n_warm, t0 = 0, time.perf_counter()
+        while n_warm < 3 or time.perf_counter() - t0 < warmup_seconds:
             torch.matmul(a, b)
+            n_warm += 1
+            if n_warm % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         reps = 30
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -262,7 +268,7 @@ def main(argv=None) -> int:
         print(f"--cache needs one of {CACHE_WORKLOADS}, the device or graph path and no window", file=sys.stderr)
         return 2
     if a.gemm_ceiling:
-        return gemm_ceiling()
+        return gemm_ceiling(a.warmup_seconds)
     if a.read_ceiling:
         return read_ceiling(a.read_ceiling)
     if a.copy_reference:
