@@ -14,14 +14,21 @@ times the same attention over a fixed-capacity KV cache instead: a step is
 the cache step (rotary on the new q/k rows, append of k/v into the cache)
 followed by the attention over the cache, both in the graph.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path graph|device|host]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-seconds S] [--workload NAME]
+                    [--path graph|device|host] [--window W] [--cache]
+    python bench.py --gemm-ceiling | --read-ceiling GIB | --copy-reference MIB
+
+Before the K timed steps it runs at least W warm-up steps and keeps going
+until S seconds (default 1) have passed: the GPU's clocks take that long to
+settle under load, and the timed steps should see the steady state.
 
 Prints ONE JSON line. ``value`` is valid-pair TFLOP/s (2 * pairs * Hq * (D + Dv)
 per step / step time) for prefill workloads and HBM GB/s (Q+K+V+O bytes per step
 / step time) for the decode workload. ``roofline`` reports the dominant
 kernel: its algorithmic work per launch over its average duration, timed with
-HIP events recorded by the library on the launch stream over the timed
-region. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
+HIP events recorded by the library on the launch stream (on the graph path
+around K eager steps of the same call, run after the warm-up and just before
+the timed replays: a graph replay records no events). ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
 same batch (rank 0, N=1).
 """
 from __future__ import annotations
