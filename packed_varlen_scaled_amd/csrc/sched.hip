@@ -74,8 +74,14 @@ __device__ Counts add(Counts a, Counts b) {
 }
 
 // Exclusive scan of one Counts per thread over the workgroup; *total gets
-// the sums. Wave prefix sums by lane shifts, then every thread adds the
-// totals of the waves before its own: two barriers.
+// the sums. Wave prefix sums by lane shifts; then every wave scans the 16
+// wave totals across its first 16 lanes (one LDS read per lane) and takes
+// the prefix of the waves before its own: two barriers.
+__device__ Counts shfl_counts(Counts c, int src) {
+  return Counts{__shfl(c.pre, src, 64), __shfl(c.decf, src, 64), __shfl(c.decp, src, 64), __shfl(c.cmb, src, 64),
+                __shfl(c.part, src, 64)};
+}
+
 __device__ Counts block_exclusive_scan(Counts v, Counts* wave_tot, Counts* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -88,13 +94,18 @@ __device__ Counts block_exclusive_scan(Counts v, Counts* wave_tot, Counts* total
   }
   if (lane == 63) wave_tot[wave] = incl;
   __syncthreads();
-  Counts before = {0, 0, 0, 0, 0}, all = {0, 0, 0, 0, 0};
-#pragma unroll 2
-  for (int w = 0; w < kWaves; ++w) {
-    const Counts t = wave_tot[w];
-    if (w < wave) before = add(before, t);
-    all = add(all, t);
+  Counts t = {0, 0, 0, 0, 0};
+  if (lane < kWaves) t = wave_tot[lane];
+#pragma unroll
+  for (int off = 1; off < kWaves; off <<= 1) {
+    const Counts o = {__shfl_up(t.pre, off, 64), __shfl_up(t.decf, off, 64), __shfl_up(t.decp, off, 64),
+                      __shfl_up(t.cmb, off, 64), __shfl_up(t.part, off, 64)};
+    if (lane >= off) t = add(t, o);
   }
+  // lane w (< kWaves) now holds the totals of waves 0..w
+  const Counts all = shfl_counts(t, kWaves - 1);
+  const Counts prev = shfl_counts(t, wave > 0 ? wave - 1 : 0);
+  const Counts before = wave > 0 ? prev : Counts{0, 0, 0, 0, 0};
   __syncthreads();  // wave_tot is reused by the next scan
   *total = all;
   return Counts{before.pre + incl.pre - v.pre, before.decf + incl.decf - v.decf, before.decp + incl.decp - v.decp,
