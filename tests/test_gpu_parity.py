@@ -581,3 +581,31 @@ def test_device_scheduler_large_batch():
     torch.cuda.synchronize()
     assert int(latch.item()) == 0
     assert torch.equal(out, want)
+
+
+def test_device_scheduler_many_items_lds_path():
+    """1500 sequences keep the scheduler's offsets in LDS, so eight workgroups
+    write the work list; with more than 16384 prefill items every
+    workgroup's item loop wraps around (decode items are there too). The
+    device-built list must give bitwise the host-scheduled result."""
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = _workload(hq=8, hkv=2, d=64)
+    rng = np.random.default_rng(12)
+    n = 1500
+    lq = [int(x) for x in rng.integers(200, 301, size=n)]
+    for i in range(0, n, 5):
+        lq[i] = 1  # decode sequences
+    lkv = [a + int(p) for a, p in zip(lq, rng.integers(0, 3000, size=n))]
+    batch = _batch(w, lq, lkv)
+    stats, _ = pva.plan(batch.cu_q, batch.cu_kv, w.num_heads, w.kv_num_heads, head_dim=w.head_dim,
+                        is_causal=True)
+    _say("device many items", stats["n_prefill_items"], stats["n_decode_items"], stats["n_combine_items"])
+    assert stats["n_prefill_items"] > 16384 and stats["n_decode_items"] > 1000
+    want = run_gpu(batch).clone()
+    ws, latch = _device_buffers(batch)
+    out = torch.full_like(want, 7.0)
+    _device_call(batch, out, ws, latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0
+    assert torch.equal(out, want)
