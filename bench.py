@@ -217,6 +217,61 @@ def gemm_ceiling(warmup_seconds: float = 1.0) -> int:
     return 0
 
 
+class ClockSampler:
+    """Graphics clock and socket power of GPU 0, polled with amdsmi from a
+    thread while it runs (used over the untimed warm-up only, so the timed
+    steps share the host with nothing). Every field is None when amdsmi is
+    not usable."""
+
+    def __init__(self, period_s: float = 0.02):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:  # no amdsmi, no device access: report nothing
+            log(f"[bench] no clock samples: {e}")
+            self._amdsmi = None
+
+    def _poll(self):
+        while not self._stop.is_set():
+            try:
+                m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+                clk, pw = m.get("current_gfxclk"), m.get("current_socket_power")
+                if isinstance(clk, (int, float)) and isinstance(pw, (int, float)):
+                    self.samples.append((float(clk), float(pw)))
+            except Exception:
+                pass
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        if self._amdsmi is not None:
+            import threading
+            self._thread = threading.Thread(target=self._poll, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        """Medians over the second half of the samples (the clocks settle first)."""
+        tail = self.samples[len(self.samples) // 2:]
+        if not tail:
+            return {"gfxclk_mhz": None, "socket_power_w": None, "samples": 0}
+        clk = sorted(c for c, _ in tail)
+        pw = sorted(w for _, w in tail)
+        return {"gfxclk_mhz": clk[len(clk) // 2], "socket_power_w": pw[len(pw) // 2], "samples": len(tail)}
+
+
 def read_ceiling(gib: float) -> int:
     """Streaming-read rate of device memory (the reference for the decode
     kernel's HBM rate): runs the read_ceiling program that the build makes,
@@ -401,7 +456,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return n
 
-    warm_steps = warm_up(step)
+    sampler = ClockSampler()
+    with sampler:
+        warm_steps = warm_up(step)
     graph = None
     graph_warm = 0
     if a.path == "graph":
@@ -423,7 +480,9 @@ def main(argv=None) -> int:
         with torch.cuda.graph(graph):
             step()
         torch.cuda.synchronize()
-        graph_warm = warm_up(graph.replay)
+        sampler = ClockSampler()
+        with sampler:
+            graph_warm = warm_up(graph.replay)
     log(f"[bench] warmup {warm_steps} steps (+{graph_warm} graph replays) done; timing {a.steps} steps ({a.path} path)")
     if graph is None:
         pva.profile_enable(True)
@@ -495,7 +554,8 @@ def main(argv=None) -> int:
         "config": {"workload": a.workload + (f" + local window {window}" if window else "")
                    + (" over a fixed-capacity KV cache (cache step + attention)" if a.cache else ""),
                    "local_window": window or None, "call": a.path, "warmup_seconds": a.warmup_seconds,
-                   "graph_warmup_replays": graph_warm, "kv_cache": cache_info, "batch": w.batch, "num_heads": w.num_heads,
+                   "graph_warmup_replays": graph_warm,
+                   "clock_during_warmup": sampler.summary(), "kv_cache": cache_info, "batch": w.batch, "num_heads": w.num_heads,
                    "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,
                    "softcap": w.softcap, "total_q": batch.total_q, "total_kv": batch.total_kv,
                    "valid_pairs": pairs, "flops_per_step": flops, "io_bytes_per_step": io_bytes,
