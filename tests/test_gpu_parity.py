@@ -216,6 +216,37 @@ def test_full_size_workloads_sampled(name):
     torch.cuda.empty_cache()
 
 
+def test_offsets_past_2_31_elements():
+    """Sequences whose Q/O and K/V element offsets lie past 2^31: a filler of
+    530000 query rows with no keys (its rows must be exactly zero) and one of
+    2.2 M keys with no queries come first, then a prefill, a tail-aligned and
+    a decode sequence, which the oracle checks. The device-scheduled call
+    must give bitwise the same output."""
+    import torch
+    w = _workload(hq=32, hkv=8, d=128)
+    lq = [530000, 0, 300, 100, 1]
+    lkv = [0, 2200000, 300, 2000, 5000]
+    _say("offsets past 2^31", lq, lkv)
+    batch = _batch(w, lq, lkv)
+    assert int(batch.cu_q[2]) * w.num_heads * w.head_dim > 2 ** 31
+    assert int(batch.cu_kv[2]) * w.kv_num_heads * w.head_dim > 2 ** 31
+    out = run_gpu(batch)
+    assert int(torch.count_nonzero(out[:lq[0]]).item()) == 0
+    picks = sample_rows(batch, [2, 3, 4], rows_per_seq=6)
+    want = oracle_sampled(batch, picks)
+    got = gather_gpu(batch, out, picks)
+    ma, rel = compare(got, want, w.dtype)
+    _say("offsets past 2^31", len(picks), "rows max_abs", ma, "rel_l2", rel)
+    ws, latch = _device_buffers(batch)
+    out2 = torch.full_like(out, 7.0)
+    _device_call(batch, out2, ws, latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0
+    assert torch.equal(out2, out)
+    del batch, out, out2, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_scores_rising_after_first_tile(dtype):
     """Keys after the first 64 score far higher (by ~40 in natural-log units)
