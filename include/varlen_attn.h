@@ -189,12 +189,14 @@ varlen_status_t varlen_attn_fwd_ex(const void* q, const void* k, const void* v,
  * and returns. It reads no host memory, allocates nothing, copies nothing
  * from the host and never synchronises, so it can be captured into a graph;
  * a replay reads the cu arrays (and q, k, v) as they are at replay time.
- * When total_q <= batch (a decode-dominated batch) the decode and combine
- * kernels run on a library-owned side stream of the device, forked from
- * `stream` after the scheduler and joined back into it before the call
+ * Usually everything runs on `stream`: the scheduler, the split-KV decode,
+ * then the prefill launch, whose last workgroups also merge the decode
+ * splits. When total_q <= batch (a decode-dominated batch) the decode and
+ * combine kernels run on a library-owned side stream of the device, forked
+ * from `stream` after the scheduler and joined back into it before the call
  * returns, so the call keeps the ordering of a single stream. The side
  * stream is created by the first such call outside a graph capture; until
- * then (and inside a capture that comes first) everything runs on `stream`.
+ * then (and inside a capture that comes first) the one-stream form runs.
  *
  *  q, k, v, out   as varlen_attn_fwd
  *  cu_seqlens_q, cu_seqlens_kv

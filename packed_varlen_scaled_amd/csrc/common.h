@@ -137,6 +137,12 @@ struct Params {
   float tanh_log2;   // 2 * scale / |softcap| * log2(e)
   float scale;       // the effective scale (fp32 path)
   float softcap;     // |softcap| (fp32 path)
+  // Device path: a prefill launch also carries the combine items. Its
+  // workgroups from prefill_grid on run combine item blockIdx.x - prefill_grid
+  // while that is below *combine_count; null combine_items: none.
+  const WorkItem* combine_items;
+  const int32_t* combine_count;
+  int32_t prefill_grid;
 };
 
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)

@@ -25,6 +25,7 @@
 // kernel stages) and the split-K decode with a partial pass and a merge pass
 // that src/kernels/group_query_attention.rs dispatches to for single-token
 // decode (backend dispatch in its run()).
+#include "combine.h"
 #include "common.h"
 
 namespace pva {
@@ -267,41 +268,11 @@ void decode_kernel(Params p, const WorkItem* __restrict__ items) {
   }
 }
 
-// One workgroup per combine item: every (row, head) of the tile merges its
-// n_splits partials in split order.
+// One workgroup per combine item.
 template <int OUT>
 __global__ __launch_bounds__(256) void combine_kernel(Params p, const WorkItem* __restrict__ items) {
   if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
-  const WorkItem it = items[blockIdx.x];
-  const int dv = p.dv;
-  const int total = it.q_rows * it.heads * dv;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int c = e % dv;
-    const int rh = e / dv;
-    const int hh = rh % it.heads;
-    const int r = rh / it.heads;
-    float M = ninf();
-    for (int s = 0; s < it.n_splits; ++s) M = fmaxf(M, p.part_lse[partial_index(it, s, r, hh)]);
-    float val = 0.f;
-    if (M != ninf()) {
-      float wsum = 0.f, acc = 0.f;
-      for (int s = 0; s < it.n_splits; ++s) {
-        const int64_t pi = partial_index(it, s, r, hh);
-        const float w = exp2_fast(p.part_lse[pi] - M);
-        wsum += w;
-        acc += w * p.part_o[pi * dv + c];
-      }
-      val = acc / wsum;
-    }
-    const int64_t tok = (int64_t)it.q_token0 + it.q_row_begin + r;
-    const int64_t oi = (tok * p.hq + it.head_begin + hh) * dv + c;
-    if constexpr (OUT == kF32) {
-      static_cast<float*>(p.out)[oi] = val;
-    } else {
-      const uint32_t w = pack2<OUT == kBF16>(val, 0.f);
-      static_cast<uint16_t*>(p.out)[oi] = (uint16_t)(w & 0xffffu);
-    }
-  }
+  combine_item<OUT>(p, items[blockIdx.x]);
 }
 
 hipError_t launch_decode(const Params& p, const WorkItem* items, int n, int dtype, hipStream_t s) {

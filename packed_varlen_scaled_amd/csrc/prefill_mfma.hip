@@ -45,6 +45,7 @@
 #include <climits>
 #include <type_traits>
 
+#include "combine.h"
 #include "common.h"
 
 namespace pva {
@@ -96,6 +97,13 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   constexpr int V0 = 2 * KS::TILE;  // first V buffer
 
+  // Device path: workgroups past the prefill grid run the combine items
+  // (their split-KV partials are complete: decode ran before this launch).
+  if (p.combine_items && (int)blockIdx.x >= p.prefill_grid) {
+    const int ci = (int)blockIdx.x - p.prefill_grid;
+    if (ci < *p.combine_count) combine_item<BF16 ? kBF16 : kF16>(p, p.combine_items[ci]);
+    return;
+  }
   if (p.item_count && (int)blockIdx.x >= *p.item_count) return;
   const WorkItem it = items[blockIdx.x];
   const int tid = threadIdx.x;

@@ -497,7 +497,8 @@ struct DeviceState {
   hipEvent_t copied = nullptr;  // after the last work-list upload
   hipEvent_t done = nullptr;    // after the last call's kernels
   bool pending = false;
-  // device path: decode + combine run on `side` beside prefill (fork/join)
+  // device path, decode-dominated batches: decode + combine run on `side`
+  // beside prefill (fork/join)
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
@@ -751,7 +752,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
                 workspace ? workspace_bytes : (size_t)0, sh.total);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  if (sh.cap_prefill > INT32_MAX || sh.cap_decode > INT32_MAX || sh.cap_partials > INT32_MAX)
+  if (sh.cap_prefill + sh.cap_combine > INT32_MAX || sh.cap_decode > INT32_MAX || sh.cap_partials > INT32_MAX)
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "the batch is too large for one launch");
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
   char* ws = static_cast<char*>(workspace);
@@ -814,15 +815,20 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
     p.tanh_log2 = 2.f * pr.scale / pr.softcap * log2e;
   }
 
-  // A decode-dominated batch (no more query rows than sequences) runs
-  // decode + combine on a side stream beside the (at most small) prefill
-  // launch: a fork after the scheduler, a join before the call returns. The
-  // decode kernel then starts right after the scheduler (measured: +2.4 % on
-  // the packed decode workload). Other batches keep one stream: there the
-  // early-exit workgroups of an empty decode launch running beside prefill
-  // would take dispatch slots from the prefill grid and shift its XCD-aware
-  // item order (measured: -2 % on the prefill workloads). The side stream
-  // and its two events are made once per device, outside any graph capture.
+  // Two launch forms.
+  //  * Decode-dominated batches (no more query rows than sequences): decode
+  //    + combine run on a side stream beside the (at most small) prefill
+  //    launch, a fork after the scheduler and a join before the call
+  //    returns, so decode starts right after the scheduler while the mostly
+  //    empty prefill grid drains beside it (measured +2.4 % on the packed
+  //    decode workload against one stream). The side stream and its two
+  //    events are made once per device, outside any graph capture.
+  //  * Other batches, on one stream: scheduler, decode, then the prefill
+  //    launch, whose workgroups past the prefill grid run the combine items
+  //    (the decode partials they merge are complete by then). That saves a
+  //    launch whose list is empty in a prefill batch. (The side form would
+  //    let an empty decode grid's early-exit workgroups take dispatch slots
+  //    beside prefill and shift its XCD-aware item order: -2 % measured.)
   std::unique_lock<std::mutex> side_lock;
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
@@ -843,7 +849,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
             ds.side = st;
             ds.fork = f;
             ds.join = j;
-          } else {  // no side stream: the kernels run one after another
+          } else {  // no side stream: the one-stream form
             if (f) (void)hipEventDestroy(f);
             if (j) (void)hipEventDestroy(j);
             if (st) (void)hipStreamDestroy(st);
@@ -857,41 +863,51 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
   }
 
   hipError_t e = timed(5, 1, stream, [&] { return pva::launch_plan(dp, cu_q_dev, cu_kv_dev, latch, stream); });
-  pva::Params pp = p;
-  auto launch_decode_combine = [&](hipStream_t s) {
-    hipError_t ee = hipSuccess;
-    if (sh.cap_decode > 0) {
-      pva::Params pd = p;
-      pd.item_count = dp.header + pva::kHdrDecode;
-      ee = timed(2, sh.cap_decode, s,
+  auto launch_decode_on = [&](hipStream_t s) {
+    if (sh.cap_decode <= 0) return hipSuccess;
+    pva::Params pd = p;
+    pd.item_count = dp.header + pva::kHdrDecode;
+    return timed(2, sh.cap_decode, s,
                  [&] { return pva::launch_decode(pd, dp.decode, (int)sh.cap_decode, pr.dtype, s); });
-    }
-    if (ee == hipSuccess && sh.cap_combine > 0) {
+  };
+  if (side) {
+    if (e == hipSuccess) e = hipEventRecord(fork_ev, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork_ev, 0);
+    if (e == hipSuccess) e = launch_decode_on(side);
+    if (e == hipSuccess && sh.cap_combine > 0) {
       pva::Params pc = p;
       pc.item_count = dp.header + pva::kHdrCombine;
-      ee = timed(3, sh.cap_combine, s,
-                 [&] { return pva::launch_combine(pc, dp.combine, (int)sh.cap_combine, pr.dtype, s); });
+      e = timed(3, sh.cap_combine, side,
+                [&] { return pva::launch_combine(pc, dp.combine, (int)sh.cap_combine, pr.dtype, side); });
     }
-    return ee;
-  };
-  if (e == hipSuccess && side) {
-    e = hipEventRecord(fork_ev, stream);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork_ev, 0);
-    if (e == hipSuccess) e = launch_decode_combine(side);
     if (e == hipSuccess) e = hipEventRecord(join_ev, side);
+  } else if (e == hipSuccess) {
+    e = launch_decode_on(stream);
   }
-  if (e == hipSuccess && sh.cap_prefill > 0) {
-    pp.item_count = dp.header + pva::kHdrPrefill;
-    if (pr.dtype == VARLEN_F32) {
+  if (e == hipSuccess && pr.dtype == VARLEN_F32) {
+    // the fp32 path has no split work (no decode items, no prefill splits)
+    if (sh.cap_combine > 0) return fail(VARLEN_ERR_DEVICE, "internal: fp32 work list with combine items");
+    if (sh.cap_prefill > 0) {
+      pva::Params pp = p;
+      pp.item_count = dp.header + pva::kHdrPrefill;
       e = timed(1, sh.cap_prefill, stream,
                 [&] { return pva::launch_prefill_f32(pp, dp.prefill, (int)sh.cap_prefill, stream); });
-    } else {
-      e = timed(0, sh.cap_prefill, stream, [&] {
-        return pva::launch_prefill_mfma(pp, dp.prefill, (int)sh.cap_prefill, pr.dtype, sh.waves, stream);
-      });
     }
+  } else if (e == hipSuccess) {
+    pva::Params pp = p;
+    pp.item_count = dp.header + pva::kHdrPrefill;
+    int64_t grid = sh.cap_prefill;
+    if (!side && sh.cap_combine > 0) {
+      pp.combine_items = dp.combine;
+      pp.combine_count = dp.header + pva::kHdrCombine;
+      pp.prefill_grid = (int32_t)sh.cap_prefill;
+      grid += sh.cap_combine;
+    }
+    if (grid > 0)
+      e = timed(0, grid, stream,
+                [&] { return pva::launch_prefill_mfma(pp, dp.prefill, (int)grid, pr.dtype, sh.waves, stream); });
   }
-  if (e == hipSuccess) e = side ? hipStreamWaitEvent(stream, join_ev, 0) : launch_decode_combine(stream);
+  if (e == hipSuccess && side) e = hipStreamWaitEvent(stream, join_ev, 0);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return VARLEN_OK;
 }
