@@ -260,6 +260,12 @@ class ClockSampler:
         if self._thread is not None:
             self._stop.set()
             self._thread.join()
+        if self._amdsmi is not None:
+            try:
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
+            self._amdsmi = None
         return False
 
     def summary(self):
