@@ -55,7 +55,8 @@ typedef enum {
   VARLEN_OK = 0,
   /* null pointer, num_heads <= 0, kv_num_heads does not divide num_heads,
    * head_dim <= 0, negative or non-finite scale, non-finite softcap, bad
-   * dtype code, total_q/total_kv out of range */
+   * dtype code, total_q/total_kv out of range, bf16/f16 q, k, v or out not
+   * 16-byte aligned */
   VARLEN_ERR_INVALID_ARGUMENT = 1,
   /* batch < 1, cu[0] != 0, a decreasing cu array, cu[batch] != total
    * ([PVA] execute(): cumulative-array validation) */
