@@ -350,8 +350,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_reference_bytes": n, "copies": 5}), flush=True)
         return 0
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the hot path is a single-GPU kernel set and this build "
-              "launches no multi-GPU work (see DESIGN.md for how it would shard). Run with --gpus 1.",
+        print("bench.py measures one GPU: the attention kernels work on one GPU's share of a batch "
+              "and the library launches no multi-GPU work. Run with --gpus 1.",
               file=sys.stderr)
         return 2
 

@@ -1,6 +1,6 @@
 """Helpers shared by the GPU parity tests: run the HIP path, run the oracle on
 the same inputs (whole batch or sampled rows of chosen sequences), compare
-with the tolerance the workloads are judged by.
+with the fixed parity tolerance per dtype.
 
 Tolerances: fp32 max|gpu - oracle| <= 1e-4; bf16 / f16 max-abs <= 2e-2 and
 ||gpu - oracle||_2 / ||oracle||_2 <= 5e-3, over every compared element.
