@@ -146,8 +146,8 @@ def attention(q, k, v, cu_q, cu_kv, num_heads: int, kv_num_heads: int | None = N
     batch = cuq.size - 1
     total_q = int(cuq[-1])
     total_kv = int(cukv[-1])
-    if total_q * hq == 0:
-        d = 1
+    if total_q * hq == 0:  # no query rows: the head size comes from K, if any
+        d = ka.size // (total_kv * hkv) if total_kv * hkv else 1
     else:
         if qa.size % (total_q * hq):
             raise ValueError("query size does not match total_q * num_heads")

@@ -1,0 +1,89 @@
+"""Seeded random attention configurations for the randomized parity sweep.
+
+Each seed draws one configuration: element type, head sizes, GQA group,
+causal or not, softcap, scale, local window and a per-sequence length mix.
+The mix draws from five kinds of sequence: single decode rows against long
+key ranges, self-attention prefill, chunked prefill after a cached past,
+more query rows than keys (the tail-aligned causal mask then fully masks the
+leading rows), and empty query ranges. The work is capped so that the fp64
+oracle finishes each case in about a second. Only shapes and options are
+drawn here; the tensors come from the seeded generators in ``synth``.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+KINDS = ("decode", "self", "chunk", "short_kv", "empty_q")
+# valid (query, key) pairs x query heads x (D + Dv), summed over the batch
+MAX_WORK = 3.0e8
+
+
+@dataclasses.dataclass(frozen=True)
+class Case:
+    seed: int
+    dtype: str
+    hq: int
+    hkv: int
+    d: int
+    dv: int
+    causal: bool
+    softcap: float
+    scale: float
+    window: int
+    lq: tuple
+    lkv: tuple
+    kinds: tuple
+
+
+def _sequence(rng, kind):
+    if kind == "decode":
+        return 1, int(rng.integers(0, 2500))
+    if kind == "self":
+        n = int(rng.integers(1, 300))
+        return n, n
+    if kind == "chunk":
+        n = int(rng.integers(1, 200))
+        return n, n + int(rng.integers(0, 800))
+    if kind == "short_kv":
+        n = int(rng.integers(2, 150))
+        return n, int(rng.integers(0, n))
+    return 0, int(rng.integers(0, 100))
+
+
+def random_case(seed: int) -> Case:
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "bf16", "bf16", "f16", "f16", "f32"][int(rng.integers(0, 6))]
+    if dtype == "f32":
+        d = int(rng.choice([16, 40, 64, 96, 128]))
+        dv = int(rng.choice([d, 48, 128]))
+    else:
+        d = int(rng.choice([64, 128]))
+        dv = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 4, 8, 16]))
+    while hkv * group > 32:
+        group //= 2
+    causal = bool(rng.integers(0, 2))
+    softcap = 0.0
+    if rng.random() < 0.4:
+        softcap = float(rng.uniform(2.0, 50.0)) * (1.0 if rng.random() < 0.8 else -1.0)
+    scale = float(rng.uniform(0.05, 0.3)) if rng.random() < 0.3 else 0.0
+    window = int(rng.integers(1, 300)) if rng.random() < 0.35 else 0
+    b = int(rng.integers(1, 9))
+    kinds = tuple(KINDS[int(rng.integers(0, len(KINDS)))] for _ in range(b))
+    lq, lkv = [], []
+    for kind in kinds:
+        a, c = _sequence(rng, kind)
+        lq.append(a)
+        lkv.append(c)
+    # halve the largest sequence's key range (and, for self-attention, its
+    # query range with it) until the oracle's work fits
+    hq = hkv * group
+    while sum(a * c for a, c in zip(lq, lkv)) * hq * (d + dv) > MAX_WORK:
+        i = int(np.argmax([a * c for a, c in zip(lq, lkv)]))
+        lkv[i] //= 2
+        if kinds[i] == "self":
+            lq[i] = lkv[i]
+    return Case(seed, dtype, hq, hkv, d, dv, causal, softcap, scale, window, tuple(lq), tuple(lkv), kinds)

@@ -474,3 +474,33 @@ def test_device_list_bounds_hold(seed):
         assert stats["n_decode_items"] <= cap_dec, (b, hq, hkv, kind, stats, cap_dec)
         assert stats["n_combine_items"] <= cap_cmb, (stats, cap_cmb)
         assert stats["n_partials"] <= cap_part, (stats, cap_part)
+
+
+# --------------------------------------------------------------------------
+# The randomized parity sweep's configurations (tests/random_cases.py).
+# --------------------------------------------------------------------------
+def test_random_cases_cover_every_option():
+    """The seeds the GPU sweep runs draw every element type, both masks,
+    softcap of either sign, a custom scale, a window, D != Dv, GQA groups
+    from 1 to 8+, and every kind of sequence."""
+    from random_cases import KINDS, random_case
+    from test_gpu_random import SEEDS
+    cases = [random_case(s) for s in SEEDS]
+    assert {c.dtype for c in cases} == {"bf16", "f16", "f32"}
+    assert {c.causal for c in cases} == {False, True}
+    assert any(c.softcap > 0 for c in cases) and any(c.softcap < 0 for c in cases)
+    assert any(c.scale > 0 for c in cases) and any(c.window > 0 for c in cases)
+    assert any(c.d != c.dv for c in cases if c.dtype != "f32") and any(c.d != c.dv for c in cases if c.dtype == "f32")
+    assert any(c.d == 128 for c in cases if c.dtype != "f32")
+    assert {c.hq // c.hkv for c in cases} >= {1, 2, 4, 8}
+    assert {k for c in cases for k in c.kinds} == set(KINDS)
+    assert any(a > b for c in cases for a, b in zip(c.lq, c.lkv)), "no sequence with L_q > L_kv"
+
+
+@pytest.mark.parametrize("seed", list(range(0, 32, 2)))
+def test_random_cases_scheduler_covers_each_visible_pair_once(seed):
+    from random_cases import random_case
+    c = random_case(seed)
+    stats, _ = _coverage(list(c.lq), list(c.lkv), c.hq, c.hkv, c.causal, dtype=c.dtype, d=c.d,
+                         window=c.window)
+    assert stats["valid_pairs"] == _brute_pairs(list(c.lq), list(c.lkv), c.causal, c.window)

@@ -129,6 +129,15 @@ def test_single_key_returns_that_value_row():
             np.testing.assert_array_equal(got[t, h], v[seq[t], h // 2].astype(np.float64))
 
 
+def test_no_query_rows_give_an_empty_output_with_the_value_head_size():
+    """A batch whose query ranges are all empty has no output rows; the value
+    head size (here different from the key head size) still shapes them."""
+    k, v = _rand((7, 2, 8)), _rand((7, 2, 12))
+    q = np.zeros((0, 4, 8), dtype=np.float32)
+    got = oracle.attention(q, k, v, [0, 0, 0], [0, 3, 7], 4, 2, dtype="f32")
+    assert got.shape == (0, 12)
+
+
 @pytest.mark.parametrize("lq,lkv", [(6, 6), (3, 9), (7, 4), (1, 5), (5, 1)])
 def test_identical_keys_give_causal_prefix_mean(lq, lkv):
     """With identical keys every visible key has the same weight, so row i is the
