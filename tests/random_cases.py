@@ -87,3 +87,13 @@ def random_case(seed: int) -> Case:
         if kinds[i] == "self":
             lq[i] = lkv[i]
     return Case(seed, dtype, hq, hkv, d, dv, causal, softcap, scale, window, tuple(lq), tuple(lkv), kinds)
+
+
+def split_options(seed: int) -> dict:
+    """Work-splitting options for a case (the result must not depend on them
+    beyond rounding): the decode path on or off, the split-KV decode chunk,
+    and the prefill key chunk."""
+    rng = np.random.default_rng(5000 + seed)
+    return dict(decode_path=int(rng.choice([0, 1, 2])),
+                decode_chunk=int(rng.choice([0, 64, 128, 200, 1000])),
+                prefill_kv_chunk=int(rng.choice([0, 0, 64, 100, 256])))

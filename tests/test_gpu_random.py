@@ -52,3 +52,21 @@ def test_random_case_matches_oracle(seed):
     torch.cuda.synchronize()
     assert int(latch.item()) == 0
     assert torch.equal(out, host), "device-scheduled call differs from the host-planned call"
+
+
+@pytest.mark.parametrize("seed", SEEDS[:48])
+def test_random_case_with_split_options_matches_oracle(seed):
+    """The same cases with the work split differently (host path): split-KV
+    decode chunks, prefill key chunks merged by the combine pass, or no
+    decode path at all."""
+    from random_cases import split_options
+    c = random_case(seed)
+    opts = split_options(seed)
+    _say("random split", c, opts)
+    w = synth.Workload(f"random{seed}", 0, c.hq, c.hkv, c.d, c.dtype, c.causal, c.softcap, c.scale, 1.0,
+                       500 + seed, c.dv)
+    batch = synth.make_batch(w, list(c.lq), list(c.lkv), device="cuda")
+    got = run_gpu(batch, local_window=c.window or None, **opts)
+    ma, rel = compare(got.double().cpu().numpy().reshape(batch.total_q, c.hq, c.dv),
+                      oracle_all(batch, local_window=c.window), c.dtype)
+    _say("random split", seed, "max_abs", ma, "rel_l2", rel)

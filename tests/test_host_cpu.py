@@ -497,10 +497,12 @@ def test_random_cases_cover_every_option():
     assert any(a > b for c in cases for a, b in zip(c.lq, c.lkv)), "no sequence with L_q > L_kv"
 
 
-@pytest.mark.parametrize("seed", list(range(0, 32, 2)))
-def test_random_cases_scheduler_covers_each_visible_pair_once(seed):
-    from random_cases import random_case
+@pytest.mark.parametrize("seed", list(range(0, 48, 3)))
+@pytest.mark.parametrize("split", [False, True])
+def test_random_cases_scheduler_covers_each_visible_pair_once(seed, split):
+    from random_cases import random_case, split_options
     c = random_case(seed)
+    opts = split_options(seed) if split else {}
     stats, _ = _coverage(list(c.lq), list(c.lkv), c.hq, c.hkv, c.causal, dtype=c.dtype, d=c.d,
-                         window=c.window)
+                         window=c.window, **opts)
     assert stats["valid_pairs"] == _brute_pairs(list(c.lq), list(c.lkv), c.causal, c.window)
