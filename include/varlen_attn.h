@@ -259,7 +259,8 @@ varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void*
  *                 elements apart (0: dense, Hkv*D and Hkv*Dv). A packed QKV
  *                 buffer [total_q, (Hq + 2 Hkv) * D] is passed as q = base,
  *                 k = base + Hq*D, v = base + (Hq + Hkv)*D with all three
- *                 strides (Hq + 2 Hkv) * D
+ *                 strides (Hq + 2 Hkv) * D. May be NULL when total_q == 0
+ *                 (no new rows: the call only writes kv_seqlens_out)
  *  k_cache, v_cache  device caches as above; new row i of sequence b goes
  *                 to row b * cache_capacity + cache_seqlens[b] + i; no other
  *                 cache row is written

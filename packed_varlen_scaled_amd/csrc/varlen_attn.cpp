@@ -1013,9 +1013,11 @@ varlen_status_t varlen_kv_append_rope(const void* q, void* q_out, const void* k,
                 (long long)qs, (long long)ks, (long long)vs);
   if (q && q_out == q && qs != (int64_t)pr.hq * pr.d)
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "in-place rotation (q_out == q) needs dense query rows");
-  if (!k || !v || !k_cache || !v_cache || !cu_seqlens_q || !cache_seqlens || !error_latch)
+  if (total_q > 0 && (!k || !v))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "k and v must be non-null when there are new rows");
+  if (!k_cache || !v_cache || !cu_seqlens_q || !cache_seqlens || !error_latch)
     return fail(VARLEN_ERR_INVALID_ARGUMENT,
-                "k, v, the caches, cu_seqlens_q, cache_seqlens and the error latch must be non-null");
+                "the caches, cu_seqlens_q, cache_seqlens and the error latch must be non-null");
   pva::RopeParams rp;
   std::memset(&rp, 0, sizeof rp);
   rp.q = q;

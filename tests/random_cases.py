@@ -97,3 +97,58 @@ def split_options(seed: int) -> dict:
     return dict(decode_path=int(rng.choice([0, 1, 2])),
                 decode_chunk=int(rng.choice([0, 64, 128, 200, 1000])),
                 prefill_kv_chunk=int(rng.choice([0, 0, 64, 100, 256])))
+
+
+@dataclasses.dataclass(frozen=True)
+class StepCase:
+    """One decode-side input step: rotate and append new rows into a cache."""
+    seed: int
+    dtype: str
+    hq: int
+    hkv: int
+    d: int
+    dv: int
+    lq: tuple
+    past: tuple
+    capacity: int
+    rotary_dim: int
+    interleaved: bool
+    opts: dict
+
+
+def random_step_case(seed: int) -> StepCase:
+    """Head sizes include ones the 16-byte kernel form cannot take (the pair
+    form runs them), rotary dims full, partial or none, position ids, packed
+    QKV row views and in-place query rotation."""
+    rng = np.random.default_rng(7000 + seed)
+    dtype = ["bf16", "bf16", "f16", "f32"][int(rng.integers(0, 4))]
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([32, 40, 64, 66, 96, 128]))
+    dv = int(rng.choice([d, 64, 72, 128]))
+    r = rng.random()
+    if r < 0.15:
+        rdim = 0
+    elif r < 0.55:
+        rdim = d
+    else:
+        rdim = 2 * int(rng.integers(1, d // 2 + 1))
+    capacity = int(rng.choice([8, 16, 64, 256]))
+    b = int(rng.integers(1, 9))
+    lq, past = [], []
+    for _ in range(b):
+        kind = int(rng.integers(0, 3))
+        n = 1 if kind == 0 else (0 if kind == 1 else int(rng.integers(1, 21)))
+        n = min(n, capacity)
+        lq.append(n)
+        past.append(int(rng.integers(0, capacity - n + 1)))
+    opts = {}
+    if rng.random() < 0.25:
+        opts["pos_ids"] = True
+    u = rng.random()
+    if u < 0.15:
+        opts["packed_qkv"] = True
+    elif u < 0.3:
+        opts["in_place"] = True
+    return StepCase(seed, dtype, hq, hkv, d, dv, tuple(lq), tuple(past), capacity, rdim, bool(rng.integers(0, 2)),
+                    opts)

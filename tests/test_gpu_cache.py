@@ -119,10 +119,22 @@ STEP_CASES = [
 
 @pytest.mark.parametrize("case", STEP_CASES, ids=[c[0] for c in STEP_CASES])
 def test_cache_step_matches_oracle(case):
+    _check_step(*case)
+
+
+@pytest.mark.parametrize("seed", list(range(64)))
+def test_random_cache_step_matches_oracle(seed):
+    """Seeded random steps (tests/random_cases.py) to the same bar."""
+    from random_cases import random_step_case
+    c = random_step_case(seed)
+    _check_step(f"random_step{seed}", c.dtype, c.hq, c.hkv, c.d, c.dv, list(c.lq), list(c.past), c.capacity,
+                c.rotary_dim, c.interleaved, c.opts, seed=300 + seed)
+
+
+def _check_step(name, dtype, hq, hkv, d, dv, lq, past, cap, rdim, inter, opts, seed=21):
     import torch
-    name, dtype, hq, hkv, d, dv, lq, past, cap, rdim, inter, opts = case
-    w = synth.Workload("custom", 0, hq, hkv, d, dtype, True, 0.0, 0.0, 1.0, 21, dv)
-    _say(name, lq, past, cap, rdim, inter, opts)
+    w = synth.Workload("custom", 0, hq, hkv, d, dtype, True, 0.0, 0.0, 1.0, seed, dv)
+    _say(name, dtype, hq, hkv, d, dv, lq, past, cap, rdim, inter, opts)
     step = synth.make_cache_step(w, lq, past, cap, device="cuda")
     kc_before = _host_bits(step.k_cache).copy()
     vc_before = _host_bits(step.v_cache).copy()

@@ -360,12 +360,12 @@ def test_device_entry_rejects_before_any_device_work(case, fragment):
 
 # ---- the cache step and the attention over a cache: host-side validation ------
 def _rope_status(batch=2, total_q=3, hq=4, hkv=2, d=64, dv=0, dtype=2, cap=16, rdim=64, rows=32, inter=0,
-                 q=1, q_out=1, qs=0, ks=0, vs=0, latch=1, cos=1):
+                 q=1, q_out=1, qs=0, ks=0, vs=0, latch=1, cos=1, kv=1):
     """varlen_kv_append_rope with dummy (never dereferenced) device pointers:
     every case here must fail validation before anything is enqueued."""
     lib = pva.load_library()
     p = lambda x: ctypes.c_void_p(x) if x else None  # noqa: E731
-    st = lib.varlen_kv_append_rope(p(q), p(q_out), p(1), p(1), qs, ks, vs, p(1), p(1), p(1), p(1), None,
+    st = lib.varlen_kv_append_rope(p(q), p(q_out), p(kv), p(kv), qs, ks, vs, p(1), p(1), p(1), p(1), None,
                                    p(cos), p(cos), None, batch, total_q, hq, hkv, d, dv, dtype, cap, rdim, rows,
                                    inter, p(latch), None)
     return st, lib.varlen_attn_last_error().decode()
@@ -385,6 +385,7 @@ def _rope_status(batch=2, total_q=3, hq=4, hkv=2, d=64, dv=0, dtype=2, cap=16, r
     (dict(ks=64), 1, "row strides"),
     (dict(q=1, q_out=1, qs=300), 1, "in-place rotation"),
     (dict(latch=0), 1, "must be non-null"),
+    (dict(kv=0), 1, "k and v must be non-null when there are new rows"),
     (dict(hq=6, hkv=4), 1, "multiple of kv_num_heads"),
     (dict(dtype=5), 1, "dtype code"),
 ])
