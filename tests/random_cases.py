@@ -152,3 +152,58 @@ def random_step_case(seed: int) -> StepCase:
         opts["in_place"] = True
     return StepCase(seed, dtype, hq, hkv, d, dv, tuple(lq), tuple(past), capacity, rdim, bool(rng.integers(0, 2)),
                     opts)
+
+
+@dataclasses.dataclass(frozen=True)
+class CacheAttnCase:
+    """Attention of new rows over a fixed-capacity cache."""
+    seed: int
+    dtype: str
+    hq: int
+    hkv: int
+    d: int
+    dv: int
+    causal: bool
+    softcap: float
+    window: int
+    lq: tuple
+    past: tuple
+    capacity: int
+
+
+def random_cache_attn_case(seed: int) -> CacheAttnCase:
+    """Decode rows, chunks after a cached past and empty query ranges over
+    caches of 64 to 3072 rows per sequence."""
+    rng = np.random.default_rng(9000 + seed)
+    dtype = ["bf16", "bf16", "f16", "f32"][int(rng.integers(0, 4))]
+    if dtype == "f32":
+        d = int(rng.choice([40, 64, 128]))
+        dv = int(rng.choice([d, 48]))
+    else:
+        d = int(rng.choice([64, 128]))
+        dv = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 4, 8, 16]))
+    while hkv * group > 32:
+        group //= 2
+    hq = hkv * group
+    causal = bool(rng.random() < 0.75)
+    softcap = 0.0
+    if rng.random() < 0.4:
+        softcap = float(rng.uniform(2.0, 50.0)) * (1.0 if rng.random() < 0.8 else -1.0)
+    window = int(rng.integers(1, 300)) if rng.random() < 0.3 else 0
+    capacity = int(rng.choice([64, 256, 1024, 3072]))
+    b = int(rng.integers(1, 9))
+    lq, past = [], []
+    for _ in range(b):
+        kind = int(rng.integers(0, 3))
+        n = 1 if kind == 0 else (0 if kind == 2 else int(rng.integers(1, min(200, capacity) + 1)))
+        lq.append(n)
+        past.append(int(rng.integers(0, capacity - n + 1)))
+    while sum(a * (a + p) for a, p in zip(lq, past)) * hq * (d + dv) > MAX_WORK:
+        i = int(np.argmax([a * (a + p) for a, p in zip(lq, past)]))
+        if past[i] > 0:
+            past[i] //= 2
+        else:
+            lq[i] //= 2
+    return CacheAttnCase(seed, dtype, hq, hkv, d, dv, causal, softcap, window, tuple(lq), tuple(past), capacity)

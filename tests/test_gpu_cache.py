@@ -255,11 +255,24 @@ def test_attention_over_cache_matches_oracle(case):
     """The new rows are copied into their slots (plain data movement), the
     attention reads the cache, and the packed call on the same rows gives the
     same bits; the unused slots hold NaN, so any read of one would show."""
+    _check_cache_attention(*case)
+
+
+@pytest.mark.parametrize("seed", list(range(48)))
+def test_random_attention_over_cache_matches_oracle(seed):
+    """Seeded random batches over caches (tests/random_cases.py), causal or
+    not, to the same bar."""
+    from random_cases import random_cache_attn_case
+    c = random_cache_attn_case(seed)
+    _check_cache_attention(f"random_cache{seed}", c.dtype, c.hq, c.hkv, c.d, c.dv, c.softcap, list(c.lq),
+                           list(c.past), c.capacity, c.window or None, causal=c.causal, seed=600 + seed)
+
+
+def _check_cache_attention(name, dtype, hq, hkv, d, dv, softcap, lq, past, cap, window, causal=True, seed=23):
     import torch
     import packed_varlen_scaled_amd as pva
-    name, dtype, hq, hkv, d, dv, softcap, lq, past, cap, window = case
-    w = synth.Workload("custom", 0, hq, hkv, d, dtype, True, softcap, 0.0, 1.0, 23, dv)
-    _say("cache attention", name, lq, past, cap, window)
+    w = synth.Workload("custom", 0, hq, hkv, d, dtype, causal, softcap, 0.0, 1.0, seed, dv)
+    _say("cache attention", name, dtype, hq, hkv, d, dv, causal, softcap, lq, past, cap, window)
     step = synth.make_cache_step(w, lq, past, cap, device="cuda")
     for b in range(len(lq)):
         s0, n = b * cap + past[b], lq[b]
@@ -272,7 +285,7 @@ def test_attention_over_cache_matches_oracle(case):
     assert int(latch.item()) == 0
     kp, cu_kv = _gather(_host_bits(step.k_cache), step.kv_len, cap)
     vp, _ = _gather(_host_bits(step.v_cache), step.kv_len, cap)
-    want = oracle.attention(_host_bits(step.q), kp, vp, step.cu_q, cu_kv, hq, hkv, is_causal=True, softcap=softcap,
+    want = oracle.attention(_host_bits(step.q), kp, vp, step.cu_q, cu_kv, hq, hkv, is_causal=causal, softcap=softcap,
                             dtype=dtype, local_window=window or 0).reshape(step.total_q, hq, w.dv)
     got = out.double().cpu().numpy().reshape(step.total_q, hq, w.dv)
     ma, rel = compare(got, want, dtype)
@@ -287,7 +300,7 @@ def test_attention_over_cache_matches_oracle(case):
     latch2 = torch.zeros(1, dtype=torch.int32, device="cuda")
     out2 = torch.empty_like(out)
     pva.varlen_attn_fwd_device(step.q, kpt, vpt, cu_q, torch.from_numpy(cu_kv).cuda(), hq, hkv,
-                               is_causal=True, softcap=softcap, local_window=window, out=out2, workspace=ws,
+                               is_causal=causal, softcap=softcap, local_window=window, out=out2, workspace=ws,
                                error_latch=latch2)
     torch.cuda.synchronize()
     assert int(latch2.item()) == 0
