@@ -615,7 +615,7 @@ def test_device_scheduler_large_batch():
 
 
 def test_device_scheduler_many_items_lds_path():
-    """1500 sequences keep the scheduler's offsets in LDS, so eight workgroups
+    """1500 sequences keep the scheduler's offsets in LDS, so eight 1024-thread workgroups
     write the work list; with more than 16384 prefill items every
     workgroup's item loop wraps around (decode items are there too). The
     device-built list must give bitwise the host-scheduled result."""
@@ -633,6 +633,28 @@ def test_device_scheduler_many_items_lds_path():
                         is_causal=True)
     _say("device many items", stats["n_prefill_items"], stats["n_decode_items"], stats["n_combine_items"])
     assert stats["n_prefill_items"] > 16384 and stats["n_decode_items"] > 1000
+    want = run_gpu(batch).clone()
+    ws, latch = _device_buffers(batch)
+    out = torch.full_like(want, 7.0)
+    _device_call(batch, out, ws, latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0
+    assert torch.equal(out, want)
+
+
+@pytest.mark.parametrize("n", [1, 255, 256, 2047, 2048])
+def test_device_scheduler_workgroup_shape_boundaries(n):
+    """Batches on both sides of each change of the scheduler's launch shape
+    (256-thread workgroups below 256 sequences, 1024-thread ones up to 2047,
+    one workgroup over the workspace from 2048): the device-built list gives
+    bitwise the host-scheduled result."""
+    import torch
+    w = _workload(hq=8, hkv=2, d=64, softcap=10.0)
+    rng = np.random.default_rng(100 + n)
+    lq = [int(x) for x in rng.choice([0, 1, 1, 3, 17, 40], size=n)]
+    lkv = [a + int(p) for a, p in zip(lq, rng.integers(0, 300, size=n))]
+    _say("device shape boundary", n, sum(lq), sum(lkv))
+    batch = _batch(w, lq, lkv)
     want = run_gpu(batch).clone()
     ws, latch = _device_buffers(batch)
     out = torch.full_like(want, 7.0)
