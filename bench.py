@@ -317,6 +317,9 @@ def main(argv=None) -> int:
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="measure the workload with a local window of W keys per row (W > 0); FLOPs count "
                          "only the pairs the window leaves visible")
+    ap.add_argument("--decode-path", type=int, default=0, choices=[0, 1],
+                    help="device and graph paths: 1 sends every sequence through the prefill kernel and "
+                         "leaves out the decode launch (for batches known to hold no single-row sequences)")
     ap.add_argument("--path", choices=["host", "device", "graph"], default="graph",
                     help="host: varlen_attn_fwd (host scheduler, host cu mirrors); device: "
                          "varlen_attn_fwd_device (device scheduler, no host work per call); graph: one "
@@ -403,7 +406,8 @@ def main(argv=None) -> int:
     def step_device():
         pva.varlen_attn_fwd_device(batch.q, batch.k, batch.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads,
                                    scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap,
-                                   local_window=window or None, out=out, workspace=ws, error_latch=latch)
+                                   local_window=window or None, out=out, workspace=ws, error_latch=latch,
+                                   decode_path=a.decode_path)
 
     step = step_host if a.path == "host" else step_device
     attn_io_bytes = io_bytes  # the attention kernels' own algorithmic bytes
@@ -559,7 +563,8 @@ def main(argv=None) -> int:
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": a.workload + (f" + local window {window}" if window else "")
                    + (" over a fixed-capacity KV cache (cache step + attention)" if a.cache else ""),
-                   "local_window": window or None, "call": a.path, "warmup_seconds": a.warmup_seconds,
+                   "local_window": window or None, "call": a.path, "decode_path": a.decode_path,
+                   "warmup_seconds": a.warmup_seconds,
                    "graph_warmup_replays": graph_warm,
                    "clock_during_warmup": sampler.summary(), "kv_cache": cache_info, "batch": w.batch, "num_heads": w.num_heads,
                    "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,

@@ -237,6 +237,31 @@ varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void*
                                        int32_t* error_latch, void* stream);
 
 /*
+ * varlen_attn_fwd_device_ex -- varlen_attn_fwd_device with the options
+ * struct, of which this path takes decode_path: 0 or 2 auto (sequences with
+ * L_q == 1 go to the split-KV decode kernel on bf16/f16), 1 never (every
+ * sequence through the prefill kernel). With 1 the decode and combine
+ * launches are left out, which suits a caller that knows its batches have
+ * no single-row sequences (a prefill-only phase); the output is the same
+ * softmax up to rounding, and bit-identical to the host-planned call with
+ * the same decode_path. decode_chunk and prefill_kv_chunk of the struct
+ * must be 0 and its local_window 0 or -1 (the window is the local_window
+ * argument), else
+ * VARLEN_ERR_INVALID_ARGUMENT; NULL options mean all zero. The workspace
+ * size of varlen_attn_device_workspace_bytes covers either decode_path.
+ * Every other argument, and the capture rules, as varlen_attn_fwd_device.
+ */
+varlen_status_t varlen_attn_fwd_device_ex(const void* q, const void* k, const void* v,
+                                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                          int32_t batch, int64_t total_q, int64_t total_kv,
+                                          int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                          int32_t v_head_dim, int32_t dtype, float scale,
+                                          int32_t is_causal, float softcap, int32_t local_window,
+                                          void* out, void* workspace, size_t workspace_bytes,
+                                          int32_t* error_latch, void* stream,
+                                          const varlen_attn_options_t* options);
+
+/*
  * varlen_kv_append_rope -- the step before a decode (or chunked-prefill) call
  * over a fixed-capacity KV cache: rotary position embedding of the new query
  * and key rows, and the append of the new key and value rows into the cache,

@@ -96,6 +96,8 @@ def load_library():
     lib.varlen_attn_fwd_device.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32, i32, f32,
                                            i32, vp, vp, ctypes.c_size_t, vp, vp]
     lib.varlen_attn_fwd_device.restype = ctypes.c_int
+    lib.varlen_attn_fwd_device_ex.argtypes = lib.varlen_attn_fwd_device.argtypes + [ctypes.POINTER(Options)]
+    lib.varlen_attn_fwd_device_ex.restype = ctypes.c_int
     lib.varlen_attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, f32, i32,
                                             f32, i32, vp, vp, ctypes.c_size_t, vp, vp]
     lib.varlen_attn_fwd_kvcache.restype = ctypes.c_int
@@ -249,13 +251,15 @@ def device_workspace_bytes(batch: int, total_q: int, total_kv: int, num_heads: i
 
 def varlen_attn_fwd_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None,
                            scale=None, is_causal: bool = False, softcap: float = 0.0, local_window=None,
-                           out=None, workspace=None, error_latch=None, stream=None):
+                           out=None, workspace=None, error_latch=None, stream=None, decode_path: int = 0):
     """The capture-safe call: cu_seqlens are read only on the device, nothing is
     allocated, copied from the host or waited for. ``workspace`` is a CUDA(HIP)
     uint8 tensor of at least ``device_workspace_bytes(...)`` bytes and
     ``error_latch`` an int32 CUDA tensor of one element, zero before first use
     (see LATCH_BITS). The rows of q/out and k/v are the buffer capacities;
-    cu_seqlens_*[-1] may be smaller. Returns ``out``."""
+    cu_seqlens_*[-1] may be smaller. decode_path=1 sends every sequence through
+    the prefill kernel and leaves out the decode and combine launches
+    (varlen_attn_fwd_device_ex). Returns ``out``."""
     import torch
     lib = load_library()
     hq = int(num_heads)
@@ -285,13 +289,18 @@ def varlen_attn_fwd_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int,
         raise ValueError("error_latch must be an int32 GPU tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
-        st = lib.varlen_attn_fwd_device(
-            q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr(),
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr(),
             cu_seqlens_q.numel() - 1, tq, tkv, hq, hkv, d, dv, code,
             float(scale) if scale else 0.0, 1 if is_causal else 0, float(softcap),
             -1 if local_window is None else int(local_window), out.data_ptr(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), error_latch.data_ptr(), stream)
+    with torch.cuda.device(q.device):
+        if decode_path:
+            opts = Options()
+            opts.decode_path = int(decode_path)
+            st = lib.varlen_attn_fwd_device_ex(*args, ctypes.byref(opts))
+        else:
+            st = lib.varlen_attn_fwd_device(*args)
     _check(st)
     return out
 

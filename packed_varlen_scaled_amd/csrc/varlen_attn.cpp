@@ -431,7 +431,7 @@ struct DeviceShape {
   size_t hdr_off = 0, seq_off = 0, pre_off = 0, dec_off = 0, cmb_off = 0, lse_off = 0, po_off = 0, total = 0;
 };
 
-DeviceShape device_shape(const Problem& pr) {
+DeviceShape device_shape(const Problem& pr, bool allow_decode = true) {
   DeviceShape d;
   const int64_t B = pr.batch;
   if (pr.dtype == VARLEN_F32) {
@@ -446,7 +446,7 @@ DeviceShape device_shape(const Problem& pr) {
     d.rows_per_item = 32 * rblocks;
     d.waves = d.nh * rblocks;
     d.nh_dec = largest_pow2_divisor_upto(pr.group, 16);
-    d.use_decode = 1;
+    d.use_decode = allow_decode ? 1 : 0;
   }
   // These bounds size the launch grids (workgroups past the device-built
   // count return at once), so they are kept tight. Prefill: every prefill
@@ -730,7 +730,8 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
                            int32_t num_heads, int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
                            int32_t dtype, float scale, int32_t is_causal, float softcap, int32_t local_window,
                            void* out, void* workspace, size_t workspace_bytes, int32_t* latch, void* stream_v,
-                           const int32_t* kv_len_dev = nullptr, int32_t kv_capacity = 0) {
+                           const int32_t* kv_len_dev = nullptr, int32_t kv_capacity = 0,
+                           bool allow_decode = true) {
   g_last_error.clear();
   Problem pr;
   varlen_status_t st = check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim,
@@ -746,7 +747,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
   if (total_kv > 0 && (!k || !v))
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "key and value pointers must be non-null");
   if ((st = check_aligned(pr, q, k, v, out)) != VARLEN_OK) return st;
-  const DeviceShape sh = device_shape(pr);
+  const DeviceShape sh = device_shape(pr, allow_decode);
   if (!workspace || workspace_bytes < sh.total)
     return fail(VARLEN_ERR_INVALID_ARGUMENT, "workspace holds %zu bytes, the call needs %zu (varlen_attn_device_workspace_bytes)",
                 workspace ? workspace_bytes : (size_t)0, sh.total);
@@ -937,7 +938,8 @@ size_t varlen_attn_device_workspace_bytes(int32_t batch, int64_t total_q, int64_
     return 0;
   pr.causal = 0;
   pr.window = 0;
-  return device_shape(pr).total;
+  // enough for either setting of decode_path (varlen_attn_fwd_device_ex)
+  return std::max(device_shape(pr).total, device_shape(pr, false).total);
 }
 
 varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
@@ -950,6 +952,29 @@ varlen_status_t varlen_attn_fwd_device(const void* q, const void* k, const void*
   return run_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv, num_heads, kv_num_heads,
                     head_dim, v_head_dim, dtype, scale, is_causal, softcap, local_window, out, workspace,
                     workspace_bytes, error_latch, stream);
+}
+
+varlen_status_t varlen_attn_fwd_device_ex(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                          const int32_t* cu_seqlens_kv, int32_t batch, int64_t total_q,
+                                          int64_t total_kv, int32_t num_heads, int32_t kv_num_heads,
+                                          int32_t head_dim, int32_t v_head_dim, int32_t dtype, float scale,
+                                          int32_t is_causal, float softcap, int32_t local_window, void* out,
+                                          void* workspace, size_t workspace_bytes, int32_t* error_latch,
+                                          void* stream, const varlen_attn_options_t* options) {
+  g_last_error.clear();
+  EntryName name("varlen_attn_fwd_device_ex");
+  const Options o = resolve_options(options);
+  if (o.decode_chunk != 0 || o.prefill_kv_chunk > 0 || (o.local_window != 0 && o.local_window != -1))
+    return fail(VARLEN_ERR_INVALID_ARGUMENT,
+                "the device-scheduled call takes only decode_path from the options (decode_chunk %d, "
+                "prefill_kv_chunk %d and options.local_window %d must be 0, or -1 for the window; the window is "
+                "an argument)",
+                o.decode_chunk, o.prefill_kv_chunk, o.local_window);
+  if (o.decode_path < 0 || o.decode_path > 2)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT, "decode_path must be 0, 1 or 2, got %d", o.decode_path);
+  return run_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv, num_heads, kv_num_heads,
+                    head_dim, v_head_dim, dtype, scale, is_causal, softcap, local_window, out, workspace,
+                    workspace_bytes, error_latch, stream, nullptr, 0, o.decode_path != 1);
 }
 
 varlen_status_t varlen_attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,

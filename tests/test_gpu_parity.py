@@ -662,3 +662,28 @@ def test_device_scheduler_workgroup_shape_boundaries(n):
     torch.cuda.synchronize()
     assert int(latch.item()) == 0
     assert torch.equal(out, want)
+
+
+@pytest.mark.parametrize("name,kw,lq,lkv,window", [c for c in DEVICE if c[1].get("dtype") != "f32"][:6],
+                         ids=[c[0] for c in DEVICE if c[1].get("dtype") != "f32"][:6])
+def test_device_call_without_decode_path(name, kw, lq, lkv, window):
+    """decode_path=1 on the device-scheduled call (varlen_attn_fwd_device_ex):
+    no decode or combine launch, every sequence through the prefill kernel;
+    bitwise the host-planned call with the same option, and the oracle."""
+    import torch
+    w = _workload(**kw)
+    _say("device no decode path", name, lq, lkv, window)
+    batch = _batch(w, lq, lkv)
+    want = run_gpu(batch, local_window=window, decode_path=1).clone()
+    ws, latch = _device_buffers(batch)
+    out = torch.full_like(want, 7.0)
+    import packed_varlen_scaled_amd as pva
+    pva.varlen_attn_fwd_device(batch.q, batch.k, batch.v, torch.from_numpy(batch.cu_q).cuda(),
+                               torch.from_numpy(batch.cu_kv).cuda(), w.num_heads, w.kv_num_heads,
+                               scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap, local_window=window,
+                               out=out, workspace=ws, error_latch=latch, decode_path=1)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0
+    assert torch.equal(out, want)
+    compare(out.double().cpu().numpy().reshape(batch.total_q, w.num_heads, w.dv),
+            oracle_all(batch, local_window=window or 0), w.dtype)

@@ -507,3 +507,18 @@ def test_random_cases_scheduler_covers_each_visible_pair_once(seed, split):
     stats, _ = _coverage(list(c.lq), list(c.lkv), c.hq, c.hkv, c.causal, dtype=c.dtype, d=c.d,
                          window=c.window, **opts)
     assert stats["valid_pairs"] == _brute_pairs(list(c.lq), list(c.lkv), c.causal, c.window)
+
+
+def test_device_ex_rejects_host_only_options_before_any_device_work():
+    lib = pva.load_library()
+    one = ctypes.c_void_p(1)
+    for kw, frag in [(dict(decode_chunk=128), "takes only decode_path"), (dict(prefill_kv_chunk=64), "takes only decode_path"),
+                     (dict(local_window=32), "takes only decode_path"), (dict(decode_path=3), "decode_path must be 0, 1 or 2")]:
+        opts = pva.Options()
+        for name, val in kw.items():
+            setattr(opts, name, val)
+        st = lib.varlen_attn_fwd_device_ex(one, one, one, one, one, 2, 16, 16, 4, 2, 64, 64, 2, 0.0, 1, 0.0, -1,
+                                           one, one, 1 << 20, one, None, ctypes.byref(opts))
+        msg = lib.varlen_attn_last_error().decode()
+        assert st == 1 and msg.startswith("varlen_attn_fwd_device_ex: ") and frag in msg, (kw, msg)
+
