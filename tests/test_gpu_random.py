@@ -85,7 +85,8 @@ def _random_lengths(rng, b, cap_q, cap_kv):
 @pytest.mark.parametrize("cfg", [
     dict(dtype="bf16", hq=16, hkv=2, d=128, dv=128, causal=True, softcap=20.0, window=None),
     dict(dtype="f16", hq=8, hkv=2, d=64, dv=128, causal=False, softcap=0.0, window=100),
-], ids=["bf16_causal_softcap", "f16_noncausal_window_dv128"])
+    dict(dtype="bf16", hq=16, hkv=2, d=128, dv=128, causal=True, softcap=0.0, window=None, decode_path=1),
+], ids=["bf16_causal_softcap", "f16_noncausal_window_dv128", "bf16_causal_no_decode_path"])
 def test_graph_replays_random_lengths(cfg):
     """One device-scheduled call captured into a HIP graph at fixed buffer
     sizes, replayed with eight seeded length sets and new data; every replay
@@ -95,6 +96,7 @@ def test_graph_replays_random_lengths(cfg):
     import torch
     import packed_varlen_scaled_amd as pva
     b, cap_q, cap_kv = 6, 800, 9000
+    dp = cfg.get("decode_path", 0)
     hq, hkv, d, dv = cfg["hq"], cfg["hkv"], cfg["d"], cfg["dv"]
     dt = synth.torch_dtype(cfg["dtype"])
     q = torch.zeros(cap_q, hq, d, dtype=dt, device="cuda")
@@ -120,9 +122,10 @@ def test_graph_replays_random_lengths(cfg):
 
     def call():
         pva.varlen_attn_fwd_device(q, k, v, cu_q, cu_kv, hq, hkv, is_causal=cfg["causal"], softcap=cfg["softcap"],
-                                   local_window=cfg["window"], out=out, workspace=ws, error_latch=latch)
+                                   local_window=cfg["window"], out=out, workspace=ws, error_latch=latch,
+                                   decode_path=dp)
 
-    rng = np.random.default_rng(77 if cfg["causal"] else 78)
+    rng = np.random.default_rng((77 if cfg["causal"] else 78) + 10 * dp)
     load(synth.make_batch(workload(90), *_random_lengths(rng, b, cap_q, cap_kv), device="cuda"))
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -138,7 +141,7 @@ def test_graph_replays_random_lengths(cfg):
     for rep in range(8):
         lq, lkv = _random_lengths(rng, b, cap_q, cap_kv)
         bt = synth.make_batch(workload(100 + rep), lq, lkv, device="cuda")
-        want = run_gpu(bt, local_window=cfg["window"]).clone()  # eager host-planned call
+        want = run_gpu(bt, local_window=cfg["window"], decode_path=dp).clone()  # eager host-planned call
         load(bt)
         out.fill_(5.0)
         torch.cuda.synchronize()
