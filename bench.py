@@ -8,28 +8,38 @@ graph, and a step is one replay: the device scheduler reads the cu arrays,
 validates them and builds the work list, then every attention kernel runs.
 --path device launches the same call eagerly each step; --path host times
 varlen_attn_fwd (host validation and scheduling, work-list upload, kernels).
-The default workload is the ragged causal prefill (B=16, L ~ U{128..2048},
-Hq=32, Hkv=8, D=128, bf16). --cache (packed_decode, chunked_prefill_cache)
-times the same attention over a fixed-capacity KV cache instead: a step is
-the cache step (rotary on the new q/k rows, append of k/v into the cache)
-followed by the attention over the cache, both in the graph.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-seconds S] [--workload NAME]
+The headline workload is the largest one that fits one GPU, the long ragged
+causal prefill with softcap 50 (B=8, L ~ logU[512,16384], Hq=64, Hkv=8,
+D=128, bf16). The same JSON line carries sub-records, measured the same way
+one after the other in this process (each batch freed before the next is
+made), for the ragged causal prefill, the chunked prefill against a cache and
+the packed decode (--only skips them). --cache (packed_decode,
+chunked_prefill_cache) times the attention over a fixed-capacity KV cache
+instead: a step is the cache step (rotary on the new q/k rows, append of k/v
+into the cache) followed by the attention over the cache, both in the graph.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-seconds S] [--workload NAME] [--only]
                     [--path graph|device|host] [--window W] [--cache]
     python bench.py --gemm-ceiling | --read-ceiling GIB | --copy-reference MIB
 
 Before the K timed steps it runs at least W warm-up steps and keeps going
 until S seconds (default 1) have passed: the GPU's clocks take that long to
-settle under load, and the timed steps should see the steady state.
+settle under load, and the timed steps should see the steady state. The JSON
+echoes W as ``warmup`` and the steps actually run as ``warmup_steps_run``.
 
 Prints ONE JSON line. ``value`` is valid-pair TFLOP/s (2 * pairs * Hq * (D + Dv)
 per step / step time) for prefill workloads and HBM GB/s (Q+K+V+O bytes per step
-/ step time) for the decode workload. ``roofline`` reports the dominant
-kernel: its algorithmic work per launch over its average duration, timed with
-HIP events recorded by the library on the launch stream (on the graph path
-around K eager steps of the same call, run after the warm-up and just before
-the timed replays: a graph replay records no events). ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
-same batch (rank 0, N=1).
+/ step time) for the decode workload; ``ms_per_step`` is the wall clock over
+the K steps between two synchronisations divided by K, and ``step_ms`` the
+median, min and max of the K steps by events on the launch stream.
+``roofline`` reports the dominant kernel: its algorithmic work per launch
+over its average duration, timed with HIP events recorded by the library on
+the launch stream (on the graph path around K eager steps of the same call,
+run after the warm-up and just before the timed replays: a graph replay
+records no events). ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample of the same batch on every CPU this process may use (capped by
+OMP_NUM_THREADS when set), and names the host CPU model.
 """
 from __future__ import annotations
 
@@ -48,7 +58,11 @@ sys.path.insert(0, ROOT)
 METRIC = "varlen attn TFLOP/s (valid pairs) + % bf16 MFMA peak; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-DEFAULT_WORKLOAD = "ragged_causal_prefill"
+# The headline is the largest configuration that fits one GPU: the long
+# ragged causal prefill with softcap. The other bf16 workloads follow in the
+# same line as sub-records (the tiny fp32 batch is a parity case only).
+DEFAULT_WORKLOAD = "long_causal_softcap"
+SUB_WORKLOADS = ("long_causal_softcap", "ragged_causal_prefill", "chunked_prefill_cache", "packed_decode")
 KERNEL_SOURCES = {
     "prefill_mfma": ["packed_varlen_scaled_amd/csrc/prefill_mfma.hip", "packed_varlen_scaled_amd/csrc/common.h"],
     "decode": ["packed_varlen_scaled_amd/csrc/decode.hip", "packed_varlen_scaled_amd/csrc/common.h"],
@@ -113,7 +127,7 @@ def cpu_baseline(batch, decode: bool, budget_s: float = 12.0, window: int = 0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the batch."""
     import oracle
     w = batch.workload
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     rng = np.random.default_rng(0)
     if decode:
         # whole sequences (every head), growing the sample until the budget is used
@@ -280,14 +294,26 @@ class ClockSampler:
 
 def read_ceiling(gib: float) -> int:
     """Streaming-read rate of device memory (the reference for the decode
-    kernel's HBM rate): runs the read_ceiling program that the build makes,
-    as a child process, before this process touches the GPU."""
+    kernel's HBM rate). The measuring program (bench_read_ceiling.hip, beside
+    this file; no part of the library) is compiled here with hipcc into a
+    temporary folder and run as a child process, before this process touches
+    the GPU."""
+    import shutil
     import subprocess
-    exe = os.path.join(ROOT, "packed_varlen_scaled_amd", "read_ceiling")
-    if not os.path.exists(exe):
-        print(f"{exe} is not built; run python -m packed_varlen_scaled_amd.build", file=sys.stderr)
-        return 1
-    res = subprocess.run([exe, str(gib)], capture_output=True, text=True)
+    import tempfile
+    src = os.path.join(ROOT, "bench_read_ceiling.hip")
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    if not os.path.exists(hipcc):
+        hipcc = shutil.which("hipcc") or "hipcc"
+    with tempfile.TemporaryDirectory() as tmp:
+        exe = os.path.join(tmp, "read_ceiling")
+        cmd = [hipcc, "-O3", "-std=c++17", "-Wall", "--offload-arch=gfx950", "-Xclang", "-target-feature",
+               "-Xclang", "-packed-fp32-ops", src, "-o", exe]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            print(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}", file=sys.stderr)
+            return 1
+        res = subprocess.run([exe, str(gib)], capture_output=True, text=True)
     for line in res.stdout.splitlines():
         log(f"[read] {line}")
     if res.returncode != 0:
@@ -300,91 +326,69 @@ def read_ceiling(gib: float) -> int:
     return 0
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--warmup-seconds", type=float, default=1.0,
-                    help="after the --warmup steps, keep running untimed steps until this many seconds have "
-                         "passed (clocks settle under load); the JSON's warmup field counts every warm-up step")
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
-                    help="only run a plain device-to-device copy of MIB mebibytes, 5 times (the known-size "
-                         "reference that HBM byte counters are calibrated against), then exit")
-    ap.add_argument("--window", type=int, default=0, metavar="W",
-                    help="measure the workload with a local window of W keys per row (W > 0); FLOPs count "
-                         "only the pairs the window leaves visible")
-    ap.add_argument("--decode-path", type=int, default=0, choices=[0, 1],
-                    help="device and graph paths: 1 sends every sequence through the prefill kernel and "
-                         "leaves out the decode launch (for batches known to hold no single-row sequences)")
-    ap.add_argument("--path", choices=["host", "device", "graph"], default="graph",
-                    help="host: varlen_attn_fwd (host scheduler, host cu mirrors); device: "
-                         "varlen_attn_fwd_device (device scheduler, no host work per call); graph: one "
-                         "device-path call captured in a HIP graph, the timed steps are replays")
-    ap.add_argument("--gemm-ceiling", action="store_true",
-                    help="only time a plain library bf16 GEMM (8192^3, torch.matmul -> hipBLASLt) on "
-                         "zero, constant and N(0,1) operands, then exit: the MFMA rate the chip sustains "
-                         "on data like the workloads', next to the dense spec peak")
-    ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="GIB",
-                    help="only run the streaming-read program over a GIB-gibibyte buffer (grid and loads in "
-                         "flight swept), then exit: the read rate device memory sustains, next to the HBM spec")
-    ap.add_argument("--cache", action="store_true",
-                    help="packed_decode / chunked_prefill_cache over a fixed-capacity KV cache: each step runs "
-                         "the cache step (rotary + append of the new rows) and the attention over the cache")
-    a = ap.parse_args(argv)
-    if a.cache and (a.workload not in CACHE_WORKLOADS or a.path == "host" or a.window):
-        print(f"--cache needs one of {CACHE_WORKLOADS}, the device or graph path and no window", file=sys.stderr)
-        return 2
-    if a.gemm_ceiling:
-        return gemm_ceiling(a.warmup_seconds)
-    if a.read_ceiling:
-        return read_ceiling(a.read_ceiling)
-    if a.copy_reference:
-        import torch
-        n = a.copy_reference << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_reference_bytes": n, "copies": 5}), flush=True)
-        return 0
-    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the attention kernels work on one GPU's share of a batch "
-              "and the library launches no multi-GPU work. Run with --gpus 1.",
-              file=sys.stderr)
-        return 2
+def host_cpu_info():
+    """Model name and logical CPU count of the host, and the CPUs this process
+    may run on (the oracle's threads)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
 
+
+def oracle_threads() -> int:
+    """Threads for the oracle: every CPU this process may run on, capped by
+    OMP_NUM_THREADS when that is set (a job's share of a shared host)."""
+    n = host_cpu_info()["usable_cpus"]
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def step_stats(ms_list):
+    """Median, min and max of per-step durations (ms)."""
+    xs = sorted(ms_list)
+    if not xs:
+        return None
+    mid = len(xs) // 2
+    med = xs[mid] if len(xs) % 2 else 0.5 * (xs[mid - 1] + xs[mid])
+    return {"median": med, "min": xs[0], "max": xs[-1], "n": len(xs)}
+
+
+def measure(name, a, cpu_budget, headline):
+    """Measure one workload; returns its record (value, unit, step times,
+    roofline of the dominant kernel, cpu_baseline, config). Every tensor it
+    made is freed before it returns."""
     import torch
     import packed_varlen_scaled_amd as pva
     import synth
 
-    if a.workload not in synth.WORKLOADS:
-        print(f"unknown workload {a.workload}; choose from {sorted(synth.WORKLOADS)}", file=sys.stderr)
-        return 2
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    pva.load_library()
-    torch.cuda.set_device(0)
-    w = synth.WORKLOADS[a.workload]
-    decode = a.workload == "packed_decode"
-    log(f"[bench] generating {a.workload} on cuda:0")
-    batch = synth.workload_batch(a.workload, device="cuda:0")
+    w = synth.WORKLOADS[name]
+    decode = name == "packed_decode"
+    window = a.window if (headline and a.window > 0) else 0
+    use_cache = headline and a.cache
+    log(f"[bench] generating {name} on cuda:0")
+    batch = synth.workload_batch(name, device="cuda:0")
     cu_q = torch.from_numpy(batch.cu_q).cuda()
     cu_kv = torch.from_numpy(batch.cu_kv).cuda()
     out = torch.empty(batch.total_q, w.num_heads, w.dv, dtype=batch.q.dtype, device="cuda:0")
-    window = a.window if a.window > 0 else 0
     pairs = pva.valid_pairs(batch.cu_q, batch.cu_kv, w.is_causal, local_window=window or None)
     flops = 2.0 * pairs * w.num_heads * (w.head_dim + w.dv)
     el = 4 if w.dtype == "f32" else 2
     io_bytes = (batch.q.numel() + batch.k.numel() + batch.v.numel() + out.numel()) * el
     if window:
         # K and V rows no query row of its sequence can see are never read
-        kv_rows = sum(b - max(0, b - a + 1 - window) if a else 0 for a, b in zip(batch.lq, batch.lkv))
+        kv_rows = sum(b - max(0, b - q + 1 - window) if q else 0 for q, b in zip(batch.lq, batch.lkv))
         io_bytes = (batch.q.numel() + out.numel()) * el + kv_rows * w.kv_num_heads * (w.head_dim + w.dv) * el
     stats, _ = pva.plan(batch.cu_q, batch.cu_kv, w.num_heads, w.kv_num_heads, head_dim=w.head_dim,
                         dtype=w.dtype, is_causal=w.is_causal, softcap=w.softcap, local_window=window or None)
@@ -412,7 +416,8 @@ def main(argv=None) -> int:
     step = step_host if a.path == "host" else step_device
     attn_io_bytes = io_bytes  # the attention kernels' own algorithmic bytes
     cache_bytes = 0
-    if a.cache:
+    cache_tensors = []
+    if use_cache:
         # The cache: each sequence's first L_kv - L_q rows are its packed K/V
         # rows; its last L_q rows are the new rows the cache step appends
         # (after turning the keys). Slots past L_kv stay unwritten.
@@ -436,7 +441,7 @@ def main(argv=None) -> int:
         q_rot = torch.empty_like(batch.q)
         ws = torch.empty(pva.device_workspace_bytes(bsz, batch.total_q, bsz * cap, w.num_heads, w.kv_num_heads,
                                                     w.head_dim, w.dv, w.dtype), dtype=torch.uint8, device="cuda:0")
-        el = 4 if w.dtype == "f32" else 2
+        cache_tensors = [kc, vc, k_new, v_new, past_t, kv_len_t, cos, sin, q_rot]
         # read q, k, v of the new rows and the two table rows; write q_out and the two cache rows
         cache_bytes = (2 * batch.total_q * (w.num_heads * w.head_dim + w.kv_num_heads * (w.head_dim + w.dv)) * el
                        + batch.total_q * w.head_dim * 4)
@@ -452,6 +457,7 @@ def main(argv=None) -> int:
                                         workspace=ws, error_latch=latch)
 
         step = step_cache
+
     def warm_up(fn):
         # W untimed steps, then more until warmup_seconds have passed: the
         # GPU's clocks take a while to settle under load (the first
@@ -496,26 +502,32 @@ def main(argv=None) -> int:
     log(f"[bench] warmup {warm_steps} steps (+{graph_warm} graph replays) done; timing {a.steps} steps ({a.path} path)")
     if graph is None:
         pva.profile_enable(True)
+    # Per-step events on the launch stream give the median / min / max; the
+    # step time itself is the wall clock over all K steps between two
+    # synchronisations.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     host_s = 0.0
-    for _ in range(a.steps):
+    evs[0].record()
+    for i in range(a.steps):
         h0 = time.perf_counter()
         if graph is None:
             step()
         else:
             graph.replay()
+        evs[i + 1].record()
         host_s += time.perf_counter() - h0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(a.steps)]
     if graph is None:
         prof = pva.profile_read()
         pva.profile_enable(False)
     else:
         prof = prof_graph
     if latch is not None and int(latch.item()) != 0:
-        log(f"[bench] error latch set: {int(latch.item())}")
-        return 1
+        raise RuntimeError(f"error latch set: {int(latch.item())}")
     ms = elapsed / a.steps * 1e3
     log(f"[bench] {ms:.4f} ms/step; host call {host_s / a.steps * 1e3:.4f} ms/step; kernels {prof}")
 
@@ -535,46 +547,155 @@ def main(argv=None) -> int:
         achieved = flops / (avg / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS}
-    traffic = load_traffic(kind, a.workload) if kind in KERNEL_SOURCES and not window and not a.cache else None
+    traffic = load_traffic(kind, name) if kind in KERNEL_SOURCES and not window and not use_cache else None
     roof["traffic"] = traffic
     roof["kernel"] = kind
     roof["kernel_avg_ms"] = avg
     roof["launches"] = k_n
 
     cache_info = None
-    if a.cache:
+    if use_cache:
         c_ms, c_n, _ = prof["cache_step"]
         c_avg = c_ms / max(c_n, 1)
         cache_info = {"kernel_avg_ms": c_avg, "bytes_per_launch": cache_bytes,
                       "GB/s": cache_bytes / (c_avg / 1e3) / 1e9 if c_avg else None,
                       "frac_of_hbm_peak": cache_bytes / (c_avg / 1e3) / 1e9 / PEAK_HBM_GBS if c_avg else None,
-                      "traffic": load_traffic("cache_step", a.workload), "capacity_rows": cap}
+                      "traffic": load_traffic("cache_step", name), "capacity_rows": cap}
         log(f"[bench] cache step {cache_info}")
 
     cpu = None
-    if not a.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(batch, decode, a.cpu_budget, window)
+    if cpu_budget > 0:
+        log(f"[bench] timing the CPU oracle on a bounded sample of {name}")
+        cpu = cpu_baseline(batch, decode, cpu_budget, window)
         log(f"[bench] cpu_baseline {cpu}")
 
-    line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": a.steps, "warmup": warm_steps,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": a.workload + (f" + local window {window}" if window else "")
-                   + (" over a fixed-capacity KV cache (cache step + attention)" if a.cache else ""),
-                   "local_window": window or None, "call": a.path, "decode_path": a.decode_path,
+    rec = {
+        "value": value, "unit": unit, "ms_per_step": ms, "step_ms": step_stats(per_step),
+        "warmup_steps_run": warm_steps, "dtype": w.dtype,
+        "config": {"workload": name + (f" + local window {window}" if window else "")
+                   + (" over a fixed-capacity KV cache (cache step + attention)" if use_cache else ""),
+                   "local_window": window or None, "call": a.path,
+                   "decode_path": a.decode_path if a.path != "host" and not use_cache else None,
                    "warmup_seconds": a.warmup_seconds,
                    "graph_warmup_replays": graph_warm,
-                   "clock_during_warmup": sampler.summary(), "kv_cache": cache_info, "batch": w.batch, "num_heads": w.num_heads,
-                   "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim, "is_causal": w.is_causal,
-                   "softcap": w.softcap, "total_q": batch.total_q, "total_kv": batch.total_kv,
-                   "valid_pairs": pairs, "flops_per_step": flops, "io_bytes_per_step": io_bytes,
+                   "clock_during_warmup": sampler.summary(), "kv_cache": cache_info, "batch": w.batch,
+                   "num_heads": w.num_heads, "kv_num_heads": w.kv_num_heads, "head_dim": w.head_dim,
+                   "is_causal": w.is_causal, "softcap": w.softcap, "total_q": batch.total_q,
+                   "total_kv": batch.total_kv, "valid_pairs": pairs, "flops_per_step": flops,
+                   "io_bytes_per_step": io_bytes,
                    "pct_of_peak": 100.0 * (value / (PEAK_HBM_GBS if decode else PEAK_BF16_TFLOPS)),
                    "host_ms_per_call": host_s / a.steps * 1e3,
                    "kernel_ms_per_step": {k: v[0] / max(a.steps, 1) for k, v in prof.items() if v[1]},
                    "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu,
+    }
+    del graph, batch, out, ws, latch, cache_tensors
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="after the --warmup steps, keep running untimed steps until this many seconds have "
+                         "passed (clocks settle under load); warmup_steps_run counts every warm-up step")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--only", action="store_true",
+                    help="measure the --workload alone (no sub-records for the other workloads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--sub-cpu-budget", type=float, default=4.0,
+                    help="seconds of oracle work for each sub-record's cpu_baseline")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB mebibytes, 5 times (the known-size "
+                         "reference that HBM byte counters are calibrated against), then exit")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="measure the workload with a local window of W keys per row (W > 0); FLOPs count "
+                         "only the pairs the window leaves visible")
+    ap.add_argument("--decode-path", type=int, default=0, choices=[0, 1],
+                    help="device and graph paths: 1 sends every sequence through the prefill kernel and "
+                         "leaves out the decode launch (for batches known to hold no single-row sequences)")
+    ap.add_argument("--path", choices=["host", "device", "graph"], default="graph",
+                    help="host: varlen_attn_fwd (host scheduler, host cu mirrors); device: "
+                         "varlen_attn_fwd_device (device scheduler, no host work per call); graph: one "
+                         "device-path call captured in a HIP graph, the timed steps are replays")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time a plain library bf16 GEMM (8192^3, torch.matmul -> hipBLASLt) on "
+                         "zero, constant and N(0,1) operands, then exit: the MFMA rate the chip sustains "
+                         "on data like the workloads', next to the dense spec peak")
+    ap.add_argument("--read-ceiling", type=float, default=0.0, metavar="GIB",
+                    help="only run the streaming-read program over a GIB-gibibyte buffer (grid and loads in "
+                         "flight swept), then exit: the read rate device memory sustains, next to the HBM spec")
+    ap.add_argument("--cache", action="store_true",
+                    help="packed_decode / chunked_prefill_cache over a fixed-capacity KV cache: each step runs "
+                         "the cache step (rotary + append of the new rows) and the attention over the cache")
+    a = ap.parse_args(argv)
+    if a.cache and (a.workload not in CACHE_WORKLOADS or a.path == "host" or a.window):
+        print(f"--cache needs one of {CACHE_WORKLOADS}, the device or graph path and no window", file=sys.stderr)
+        return 2
+    if a.decode_path and (a.path == "host" or a.cache):
+        print("--decode-path applies to the device and graph paths without --cache (the host path and the "
+              "cache call always use the automatic setting)", file=sys.stderr)
+        return 2
+    if a.steps < 1:
+        print("--steps must be at least 1", file=sys.stderr)
+        return 2
+    if a.gemm_ceiling:
+        return gemm_ceiling(a.warmup_seconds)
+    if a.read_ceiling:
+        return read_ceiling(a.read_ceiling)
+    if a.copy_reference:
+        import torch
+        n = a.copy_reference << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes": n, "copies": 5}), flush=True)
+        return 0
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the attention kernels work on one GPU's share of a batch "
+              "and the library launches no multi-GPU work. Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import packed_varlen_scaled_amd as pva
+    import synth
+
+    if a.workload not in synth.WORKLOADS:
+        print(f"unknown workload {a.workload}; choose from {sorted(synth.WORKLOADS)}", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pva.load_library()
+    torch.cuda.set_device(0)
+
+    head = measure(a.workload, a, 0.0 if a.no_cpu_baseline else a.cpu_budget, headline=True)
+    subs = None
+    if not (a.only or a.cache or a.window):
+        subs = {}
+        for name in SUB_WORKLOADS:
+            if name == a.workload:
+                continue
+            subs[name] = measure(name, a, 0.0 if a.no_cpu_baseline else a.sub_cpu_budget, headline=False)
+
+    cpu = head["cpu_baseline"]
+    if cpu is not None:
+        cpu = dict(cpu, host=host_cpu_info())
+    line = {
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "warmup_steps_run": head["warmup_steps_run"],
+        "ms_per_step": head["ms_per_step"], "step_ms": head["step_ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+        "config": head["config"], "roofline": head["roofline"], "cpu_baseline": cpu,
+        "sub_records": subs,
     }
     print(json.dumps(line), flush=True)
     return 0

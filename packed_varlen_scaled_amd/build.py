@@ -28,10 +28,6 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIP_SOURCES = ["prefill_mfma.hip", "decode.hip", "prefill_f32.hip", "sched.hip", "rope_append.hip"]
 HOST_SOURCES = ["varlen_attn.cpp"]
-# A standalone measurement program (not part of the library): the streaming
-# read rate of device memory, which bench.py --read-ceiling runs.
-READ_CEILING_SRC = "read_ceiling.hip"
-READ_CEILING_PATH = os.path.join(HERE, "read_ceiling")
 ARCH = "gfx950"
 
 
@@ -109,19 +105,7 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     with open(RESOURCES_PATH + ".tmp", "w") as f:
         json.dump(resources, f, indent=1)
     os.replace(RESOURCES_PATH + ".tmp", RESOURCES_PATH)
-    _build_read_ceiling(verbose)
     return LIB_PATH
-
-
-def _build_read_ceiling(verbose: bool) -> None:
-    tmp = READ_CEILING_PATH + ".tmp%d" % os.getpid()
-    cmd = [_hipcc(), "-O3", "-std=c++17", "-Wall"] + DEVICE + [os.path.join(CSRC, READ_CEILING_SRC), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed on {READ_CEILING_SRC}:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, READ_CEILING_PATH)
 
 
 def undefined_kernel_stubs(lib_path: str):

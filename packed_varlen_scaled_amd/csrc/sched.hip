@@ -231,10 +231,18 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
       if (!cache && akv[B] > dp.cap_kv) err |= kLatchCuKvTotal;
     }
     for (int32_t b = tid; b < B; b += kThreads) {
+      // Order is tested on the elements themselves, never on a difference:
+      // a difference of two int32 can wrap (e.g. INT32_MIN - INT32_MAX) and
+      // look non-negative. With cu[0] == 0, no decrease and cu[B] <= the
+      // buffer's rows, every element lies in [0, rows] and the differences
+      // taken below cannot wrap.
+      const bool q_bad = aq[b + 1] < aq[b];
+      const bool kv_bad = cache ? (akv[b] < 0 || akv[b] > dp.kv_capacity) : akv[b + 1] < akv[b];
+      if (q_bad) err |= kLatchCuQOrder;
+      if (kv_bad) err |= cache ? kLatchKvLen : kLatchCuKvOrder;
+      if (q_bad || kv_bad) continue;
       const int32_t lq = aq[b + 1] - aq[b];
       const int32_t lkv = lkv_of(b);
-      if (lq < 0) err |= kLatchCuQOrder;
-      if (cache ? (lkv < 0 || lkv > dp.kv_capacity) : lkv < 0) err |= cache ? kLatchKvLen : kLatchCuKvOrder;
       const bool dec = dp.use_decode && lq == 1;
       if (dec && lkv > 0) dec_keys += lkv;
       has_dec |= dec;

@@ -503,6 +503,10 @@ struct DeviceState {
   hipEvent_t fork = nullptr, join = nullptr;
 };
 
+// New capacity of a grow-only buffer that holds `old_cap` bytes and must
+// hold `need`: at least twice the old capacity.
+size_t grown_capacity(size_t old_cap, size_t need) { return std::max(need, old_cap * 2); }
+
 constexpr int kMaxDevices = 64;
 DeviceState g_dev[kMaxDevices];
 
@@ -636,24 +640,26 @@ varlen_status_t run(const void* q, const void* k, const void* v, const int32_t* 
     PVA_HIP(hipStreamWaitEvent(stream, ds.done, 0), "ordering after the previous call");
   }
   const size_t item_bytes = lay.n_items * sizeof(WorkItem);
+  // Both buffers grow to at least twice their previous size, so a run of
+  // slightly larger calls reallocates O(log n) times, not once per call.
   if (lay.total > ds.dev_cap) {
+    const size_t cap = grown_capacity(ds.dev_cap, lay.total);
     if (ds.dev) {
       PVA_HIP(hipEventSynchronize(ds.done), "waiting before growing the workspace");
       PVA_HIP(hipFree(ds.dev), "hipFree");
       ds.dev = nullptr;
       ds.dev_cap = 0;
     }
-    const size_t cap = std::max(lay.total, ds.dev_cap * 2);
     PVA_HIP(hipMalloc(&ds.dev, cap), "allocating the workspace");
     ds.dev_cap = cap;
   }
   if (item_bytes > ds.host_cap) {
+    const size_t cap = grown_capacity(ds.host_cap, item_bytes);
     if (ds.host) {
       PVA_HIP(hipHostFree(ds.host), "hipHostFree");
       ds.host = nullptr;
       ds.host_cap = 0;
     }
-    const size_t cap = std::max(item_bytes, ds.host_cap * 2);
     PVA_HIP(hipHostMalloc(&ds.host, cap, hipHostMallocDefault), "allocating the pinned staging buffer");
     ds.host_cap = cap;
   }

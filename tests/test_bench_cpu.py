@@ -64,3 +64,39 @@ def test_cpu_baseline_record(decode):
     assert set(rec) == {"value", "unit", "cores", "kind", "sample"}
     assert rec["kind"] == "oracle" and rec["cores"] >= 1 and rec["value"] > 0
     assert rec["unit"] == ("GB/s" if decode else "TFLOP/s")
+
+
+def test_step_stats_median_min_max():
+    assert bench.step_stats([3.0, 1.0, 2.0]) == {"median": 2.0, "min": 1.0, "max": 3.0, "n": 3}
+    assert bench.step_stats([4.0, 1.0, 2.0, 3.0])["median"] == 2.5
+    assert bench.step_stats([]) is None
+
+
+def test_host_cpu_info_and_oracle_threads(monkeypatch):
+    info = bench.host_cpu_info()
+    assert set(info) == {"model", "logical_cpus", "usable_cpus"}
+    assert info["usable_cpus"] >= 1
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.oracle_threads() == 1
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.oracle_threads() == info["usable_cpus"]
+
+
+@pytest.mark.parametrize("args", [["--decode-path", "1", "--path", "host"],
+                                  ["--decode-path", "1", "--cache", "--workload", "packed_decode"]])
+def test_decode_path_refused_where_it_would_be_ignored(args, capsys):
+    assert bench.main(args) == 2
+    assert "--decode-path" in capsys.readouterr().err
+
+
+def test_headline_is_the_largest_workload_and_sub_records_cover_the_rest():
+    sizes = {}
+    for name in bench.SUB_WORKLOADS:
+        w = synth.WORKLOADS[name]
+        lq, lkv = synth.draw_lengths(name)
+        if name == "packed_decode":
+            continue
+        pairs = pva.valid_pairs(synth.cu_seqlens(lq), synth.cu_seqlens(lkv), w.is_causal)
+        sizes[name] = 2.0 * pairs * w.num_heads * (w.head_dim + w.dv)
+    assert bench.DEFAULT_WORKLOAD == max(sizes, key=sizes.get)
+    assert set(bench.SUB_WORKLOADS) == set(synth.WORKLOADS) - {"tiny_fp32"}

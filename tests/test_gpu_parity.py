@@ -478,6 +478,33 @@ def test_device_scheduler_latches_bad_cu_seqlens():
     assert int(latch.item()) == 0 and torch.equal(out, run_gpu(batch))
 
 
+def test_device_scheduler_latches_cu_arrays_whose_differences_wrap():
+    """A decreasing cu array whose int32 differences wrap to non-negative
+    values (INT32_MIN - INT32_MAX == 1) is latched as out of order and nothing
+    is computed."""
+    import torch
+    w = _workload(hq=8, hkv=2)
+    batch = _batch(w, [20, 20, 20, 10], [20, 20, 20, 10])
+    ws, latch = _device_buffers(batch)
+    sentinel = torch.full((batch.total_q, 8, 128), 3.0, dtype=batch.q.dtype, device="cuda")
+    imax, imin = 2**31 - 1, -2**31
+    good = [0, 20, 40, 60, 70]
+    for cq, ckv, bit in [([0, imax, imin, -1, 70], good, 2), (good, [0, imax, imin, -1, 70], 16),
+                         ([0, imax, imin, imin + 1, 70], good, 2), ([0, imax, imin, -1, 70], [0, imax, imin, -1, 70], 18)]:
+        _say("wrap latch", cq, ckv, bit)
+        latch.zero_()
+        out = sentinel.clone()
+        _device_call(batch, out, ws, latch, cu_q=torch.tensor(cq, dtype=torch.int32, device="cuda"),
+                     cu_kv=torch.tensor(ckv, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        assert int(latch.item()) == bit
+        assert torch.equal(out, sentinel)
+    latch.zero_()
+    _device_call(batch, out, ws, latch)
+    torch.cuda.synchronize()
+    assert int(latch.item()) == 0 and torch.equal(out, run_gpu(batch))
+
+
 def test_graph_capture_replays_with_new_lengths():
     """Capture one call into a HIP graph, then replay it with new cu_seqlens
     (fewer or more rows inside the same buffers) and new data: every replay
