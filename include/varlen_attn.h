@@ -262,6 +262,39 @@ varlen_status_t varlen_attn_fwd_device_ex(const void* q, const void* k, const vo
                                           const varlen_attn_options_t* options);
 
 /*
+ * varlen_attn_fwd_device_noalloc -- varlen_attn_fwd_device for callers that
+ * cannot allocate device memory at all, not even a workspace of their own:
+ * code under HIP-graph capture that must not call hipMalloc, tight serving
+ * loops, harnesses that forbid allocation. It takes the same arguments
+ * without the workspace and behaves like varlen_attn_fwd_device with default
+ * options, with the same kernels on the same items (bitwise the same
+ * output), always in the one-stream form (no side stream).
+ *
+ * The work list and split-KV partials live in a static device array of
+ * VARLEN_NOALLOC_SCRATCH_BYTES bytes inside the library, of which every GPU
+ * the library runs on holds its own copy until the process ends (its device
+ * address is looked up on the first such call on a GPU). The call allocates
+ * nothing: no hipMalloc, hipFree, stream or event (kernel timing through
+ * varlen_attn_profile_enable does not record this call). A batch whose work
+ * list needs more than that many bytes (the size varlen_attn_device_workspace_
+ * bytes reports, e.g. about 25 MB for 256 decode rows against 4.2 M keys)
+ * returns VARLEN_ERR_INVALID_ARGUMENT before anything is enqueued. Every
+ * such call on one GPU shares the one array, and each call overwrites it:
+ * calls that overlap on a GPU (different streams, threads or captured graphs
+ * in flight at once) race and must be serialised by the caller. Nothing in
+ * the array needs to be cleared between calls.
+ */
+#define VARLEN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+varlen_status_t varlen_attn_fwd_device_noalloc(const void* q, const void* k, const void* v,
+                                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                               int32_t batch, int64_t total_q, int64_t total_kv,
+                                               int32_t num_heads, int32_t kv_num_heads, int32_t head_dim,
+                                               int32_t v_head_dim, int32_t dtype, float scale,
+                                               int32_t is_causal, float softcap, int32_t local_window,
+                                               void* out, int32_t* error_latch, void* stream);
+
+/*
  * varlen_kv_append_rope -- the step before a decode (or chunked-prefill) call
  * over a fixed-capacity KV cache: rotary position embedding of the new query
  * and key rows, and the append of the new key and value rows into the cache,

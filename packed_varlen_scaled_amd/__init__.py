@@ -98,6 +98,9 @@ def load_library():
     lib.varlen_attn_fwd_device.restype = ctypes.c_int
     lib.varlen_attn_fwd_device_ex.argtypes = lib.varlen_attn_fwd_device.argtypes + [ctypes.POINTER(Options)]
     lib.varlen_attn_fwd_device_ex.restype = ctypes.c_int
+    lib.varlen_attn_fwd_device_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i32, i32, f32,
+                                                   i32, f32, i32, vp, vp, vp]
+    lib.varlen_attn_fwd_device_noalloc.restype = ctypes.c_int
     lib.varlen_attn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, i32, i32, i32, f32, i32,
                                             f32, i32, vp, vp, ctypes.c_size_t, vp, vp]
     lib.varlen_attn_fwd_kvcache.restype = ctypes.c_int
@@ -301,6 +304,55 @@ def varlen_attn_fwd_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int,
             st = lib.varlen_attn_fwd_device_ex(*args, ctypes.byref(opts))
         else:
             st = lib.varlen_attn_fwd_device(*args)
+    _check(st)
+    return out
+
+
+# Bytes of the static scratch array behind varlen_attn_fwd_device_noalloc
+# (VARLEN_NOALLOC_SCRATCH_BYTES in include/varlen_attn.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def varlen_attn_fwd_device_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_kv, num_heads: int, kv_num_heads=None,
+                                   scale=None, is_causal: bool = False, softcap: float = 0.0, local_window=None,
+                                   out=None, error_latch=None, stream=None):
+    """varlen_attn_fwd_device without a workspace argument: the library's
+    static scratch array (NOALLOC_SCRATCH_BYTES per GPU) holds the work list,
+    so the call allocates nothing at all. Calls that overlap on one GPU share
+    that array and race. Arguments as varlen_attn_fwd_device. Returns ``out``."""
+    import torch
+    lib = load_library()
+    hq = int(num_heads)
+    hkv = int(kv_num_heads) if kv_num_heads else hq
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("Q, K, and V must use the same floating dtype")
+    tq, d = _resolve(q, hq, "query")
+    tkv, dk = _resolve(k, hkv, "key")
+    tv, dv = _resolve(v, hkv, "value")
+    if dk != d or tv != tkv:
+        raise ValueError("key head size / token count must match query head size / value token count")
+    if out is None:
+        raise ValueError("out is required (the call allocates nothing)")
+    if out.dtype != q.dtype or not out.is_contiguous() or out.numel() != tq * hq * dv or not out.is_cuda:
+        raise ValueError("output must be a contiguous GPU tensor of the Q/K/V dtype with [total_q, num_heads, v_head_size] elements")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if cu is None or not cu.is_cuda or cu.dtype != torch.int32 or not cu.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_kv.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_kv lengths differ")
+    if error_latch is None or not error_latch.is_cuda or error_latch.dtype != torch.int32:
+        raise ValueError("error_latch must be an int32 GPU tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib.varlen_attn_fwd_device_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_kv.data_ptr(),
+            cu_seqlens_q.numel() - 1, tq, tkv, hq, hkv, d, dv, code, float(scale) if scale else 0.0,
+            1 if is_causal else 0, float(softcap), -1 if local_window is None else int(local_window),
+            out.data_ptr(), error_latch.data_ptr(), stream)
     _check(st)
     return out
 

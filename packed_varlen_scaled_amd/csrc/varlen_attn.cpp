@@ -33,6 +33,18 @@ hipError_t launch_rope_append(const RopeParams& p, int dtype, hipStream_t s);
 int rope_units_per_block(int vec);
 }  // namespace pva
 
+// Scratch of the allocation-free call (varlen_attn_fwd_device_noalloc): the
+// device-built work list and the split-KV partials of one call, in a static
+// array of which every GPU the library runs on holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, not a
+// device address: the device address of the current GPU's copy comes from
+// hipGetSymbolAddress (noalloc_scratch below) and only that address is
+// passed to kernels. Nothing in it has to start at zero (the scheduler writes
+// the list header on every call, and partials are written before they are
+// read). Every such call on one GPU shares the array, so calls that overlap
+// on a GPU (other streams, other threads) race.
+static __device__ __align__(256) unsigned char scratch[VARLEN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using pva::WorkItem;
@@ -501,6 +513,9 @@ struct DeviceState {
   // beside prefill (fork/join)
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // device address of this GPU's copy of `scratch` (the allocation-free
+  // call), looked up once; the memory lives until the process ends
+  void* scratch = nullptr;
 };
 
 // New capacity of a grow-only buffer that holds `old_cap` bytes and must
@@ -513,6 +528,10 @@ DeviceState g_dev[kMaxDevices];
 // ---------------------------------------------------------------------------
 // Optional kernel timing (HIP events around each launch, on its stream).
 // ---------------------------------------------------------------------------
+// Set for the duration of varlen_attn_fwd_device_noalloc on its thread: no
+// timing events are made or recorded (an event pool may have to grow).
+thread_local bool g_no_alloc_call = false;
+
 struct ProfRecord {
   int kind;
   int64_t items;
@@ -543,7 +562,7 @@ hipError_t timed(int kind, int64_t items, hipStream_t s, F&& launch) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     on = g_prof_on;
   }
-  if (!on || items <= 0) return launch();
+  if (!on || items <= 0 || g_no_alloc_call) return launch();
   hipEvent_t a, b;
   {
     std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -737,7 +756,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
                            int32_t dtype, float scale, int32_t is_causal, float softcap, int32_t local_window,
                            void* out, void* workspace, size_t workspace_bytes, int32_t* latch, void* stream_v,
                            const int32_t* kv_len_dev = nullptr, int32_t kv_capacity = 0,
-                           bool allow_decode = true) {
+                           bool allow_decode = true, bool no_alloc = false) {
   g_last_error.clear();
   Problem pr;
   varlen_status_t st = check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim,
@@ -836,10 +855,12 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
   //    launch whose list is empty in a prefill batch. (The side form would
   //    let an empty decode grid's early-exit workgroups take dispatch slots
   //    beside prefill and shift its XCD-aware item order: -2 % measured.)
+  // The allocation-free call always takes the one-stream form: making the
+  // side stream and its events would allocate.
   std::unique_lock<std::mutex> side_lock;
   hipStream_t side = nullptr;
   hipEvent_t fork_ev = nullptr, join_ev = nullptr;
-  if (sh.cap_prefill > 0 && sh.cap_decode > 0 && total_q <= batch) {
+  if (!no_alloc && sh.cap_prefill > 0 && sh.cap_decode > 0 && total_q <= batch) {
     int dev_id = 0;
     PVA_HIP(hipGetDevice(&dev_id), "hipGetDevice");
     if (dev_id >= 0 && dev_id < kMaxDevices) {
@@ -919,6 +940,31 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
   return VARLEN_OK;
 }
 
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device (the first allocation-free call on it).
+varlen_status_t noalloc_scratch(void** ptr) {
+  int dev_id = 0;
+  PVA_HIP(hipGetDevice(&dev_id), "hipGetDevice");
+  if (dev_id < 0 || dev_id >= kMaxDevices) return fail(VARLEN_ERR_DEVICE, "device index %d out of range", dev_id);
+  DeviceState& ds = g_dev[dev_id];
+  std::lock_guard<std::mutex> lock(ds.mu);
+  if (!ds.scratch) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(VARLEN_ERR_DEVICE, "hipGetSymbolAddress(scratch) gave a null address");
+    ds.scratch = p;
+  }
+  *ptr = ds.scratch;
+  return VARLEN_OK;
+}
+
+// Clears the allocation-free flag when the call returns.
+struct NoAllocCall {
+  NoAllocCall() { g_no_alloc_call = true; }
+  ~NoAllocCall() { g_no_alloc_call = false; }
+};
+
 }  // namespace
 
 extern "C" {
@@ -981,6 +1027,33 @@ varlen_status_t varlen_attn_fwd_device_ex(const void* q, const void* k, const vo
   return run_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv, num_heads, kv_num_heads,
                     head_dim, v_head_dim, dtype, scale, is_causal, softcap, local_window, out, workspace,
                     workspace_bytes, error_latch, stream, nullptr, 0, o.decode_path != 1);
+}
+
+varlen_status_t varlen_attn_fwd_device_noalloc(const void* q, const void* k, const void* v,
+                                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                               int32_t batch, int64_t total_q, int64_t total_kv, int32_t num_heads,
+                                               int32_t kv_num_heads, int32_t head_dim, int32_t v_head_dim,
+                                               int32_t dtype, float scale, int32_t is_causal, float softcap,
+                                               int32_t local_window, void* out, int32_t* error_latch,
+                                               void* stream) {
+  g_last_error.clear();
+  EntryName name("varlen_attn_fwd_device_noalloc");
+  NoAllocCall no_alloc;
+  Problem pr;
+  varlen_status_t st = check_scalars(batch, total_q, total_kv, num_heads, kv_num_heads, head_dim, v_head_dim,
+                                     dtype, scale, softcap, &pr);
+  if (st != VARLEN_OK) return st;
+  const size_t need = device_shape(pr).total;
+  if (need > (size_t)VARLEN_NOALLOC_SCRATCH_BYTES)
+    return fail(VARLEN_ERR_INVALID_ARGUMENT,
+                "this batch needs %zu bytes of scratch and the allocation-free call holds %zu "
+                "(VARLEN_NOALLOC_SCRATCH_BYTES); call varlen_attn_fwd_device with a workspace instead",
+                need, (size_t)VARLEN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != VARLEN_OK) return st;
+  return run_device(q, k, v, cu_seqlens_q, cu_seqlens_kv, batch, total_q, total_kv, num_heads, kv_num_heads,
+                    head_dim, v_head_dim, dtype, scale, is_causal, softcap, local_window, out, ws,
+                    (size_t)VARLEN_NOALLOC_SCRATCH_BYTES, error_latch, stream, nullptr, 0, true, true);
 }
 
 varlen_status_t varlen_attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
