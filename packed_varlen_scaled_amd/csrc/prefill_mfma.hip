@@ -47,40 +47,9 @@
 
 #include "combine.h"
 #include "common.h"
+#include "prefill_tiles.h"
 
 namespace pva {
-
-enum TileMode : int { kFirst = 0, kPlain = 1, kMasked = 2, kSafe = 3 };
-
-// LDS chunk swizzle: 16-byte chunk c of key row r is stored at chunk
-// c ^ chunk_perm<D>(r). gfx950's LDS serves 64 banks of 4 bytes per clock, so
-// a 128-dim bf16 row (256 bytes) spans the banks exactly once and a 64-dim row
-// half of them. The permutation makes both access patterns of the kernel
-// conflict-free: 16 consecutive rows at one logical chunk (the K fragment
-// reads) and 4 consecutive rows x 4 consecutive chunks (the transpose reads
-// of V).
-template <int D>
-__device__ __forceinline__ int chunk_perm(int r) {
-  if constexpr (D == 128) {
-    return 4 * (r & 3) + ((r >> 2) & 3);
-  } else {
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-  }
-}
-
-// Tile geometry of one operand with rows of W 16-bit elements: a wave's 1 KB
-// load covers 512 / W key rows, a 64-key tile splits into 1 KB blocks dealt
-// round-robin to the NW waves.
-template <int W, int NW>
-struct TileShape {
-  static constexpr int BN = 64;
-  static constexpr int CH = W / 8;               // 16-byte chunks per key row
-  static constexpr int TILE = BN * W;            // 16-bit elements per tile
-  static constexpr int ROWS_PER_BLOCK = 512 / W;
-  static constexpr int BLOCKS = BN / ROWS_PER_BLOCK;
-  static constexpr int BPW = BLOCKS / NW;        // 1 KB blocks per wave per tile
-  static_assert(BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
-};
 
 template <int D, int DV, bool BF16, int NW, bool SOFTCAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -130,6 +99,14 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const int kv_begin = it.kv_begin;
   const int kv_end = it.kv_end;
   const int64_t tok = (int64_t)it.q_token0 + it.q_row_begin + my_row;
+  // Short-series softcap (see the tile body): x = a * cap_k for a raw score
+  // a; usable while |a| <= cap_short_lim (|x| <= 1/4, and a within f16).
+  // The series is even in x, so a negative cap takes it too.
+  const float cap_kf = SOFTCAP ? p.scale / p.softcap : 0.f;
+  const float cap_short_lim = SOFTCAP ? fminf(0.25f / __builtin_fabsf(cap_kf), 32768.f) : 0.f;
+  const f16x2_t cap_k = {(_Float16)cap_kf, (_Float16)cap_kf};
+  const f16x2_t cap_c1 = {(_Float16)(-1.f / 3.f), (_Float16)(-1.f / 3.f)};
+  const f16x2_t cap_c2 = {(_Float16)(2.f / 15.f), (_Float16)(2.f / 15.f)};
 
   // Q fragments, the B operand of S^T = K Q^T: lane l supplies query row
   // l%32 at head dims 16*kk + 8*half + 0..7.
@@ -252,6 +229,28 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     // sacc[mt][r] is the score of query row l32 and key
     // kt + 32*mt + 8*(r/4) + 4*half + r%4.
 
+    // ---- softcap: short-series form when every score of the tile is small ----
+    // With x = s / c (s = scale * q.k, c the softcap), c tanh(x) = s (1 + t)
+    // with t = -x^2/3 + 2 x^4/15 - 17 x^6/315 + ... For |x| <= 1/4 the first
+    // two terms leave a relative error below 1.3e-5, and t is small enough
+    // (|t| <= 0.021) to be formed in packed f16: its own f16 rounding then
+    // moves the score by less than 2^-9 of a unit in log2 scale, well under
+    // the bf16 rounding of P. This takes one transcendental per score instead
+    // of three (2^x, reciprocal, 2^x). The form is chosen per wave and tile:
+    // every raw score of the wave's tile (masked ones included, taken before
+    // the mask) must lie within the bound, else the tile takes the exact
+    // form. The bound also keeps the raw scores inside f16's range.
+    bool short_cap = false;
+    if constexpr (SOFTCAP && (MODE == kPlain || MODE == kMasked)) {
+      float mx = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < BN / 32; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, __builtin_fabsf(sacc[mt][r])), __builtin_fabsf(sacc[mt][r + 1]));
+      }
+      short_cap = !__any(!(mx <= cap_short_lim));
+    }
+
     // ---- mask and tile max ---------------------------------------------------
     if constexpr (MASK) {
       // Register r of sacc[mt] holds key kt + 4*half + c with the constant
@@ -332,21 +331,44 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     const float m_use = (m_ref == ninf()) ? 0.f : m_ref;
 
     // ---- P = 2^(y - m_use) -----------------------------------------------------
+    if (short_cap) {
+      // y = score_log2 * a * (1 + t), a the raw score, t from x = a * scale / c
+      // in packed f16 (a masked score is -inf and gives P = 0 either way)
 #pragma unroll
-    for (int mt = 0; mt < BN / 32; ++mt) {
+      for (int mt = 0; mt < BN / 32; ++mt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float s = sacc[mt][r];
-        float pr;
-        if constexpr (SOFTCAP) {
-          const float t = exp2_fast(s * p.tanh_log2);
-          const float rr = rcp_fast(t + 1.f);
-          pr = exp2_fast(__builtin_fmaf(rr, -2.f * p.cap_log2, p.cap_log2 - m_use));
-          if constexpr (MASK) pr = (s == ninf()) ? 0.f : pr;
-        } else {
-          pr = exp2_fast(__builtin_fmaf(s, p.score_log2, -m_use));
+        for (int r = 0; r < 16; r += 2) {
+          const float a0 = sacc[mt][r], a1 = sacc[mt][r + 1];
+          const f16x2_t x = __builtin_convertvector(f32x2_t{a0, a1}, f16x2_t) * cap_k;
+          const f16x2_t u = x * x;
+          const f16x2_t t = u * (u * cap_c2 + cap_c1);
+          float pr0 = exp2_fast(__builtin_fmaf(__builtin_fmaf(a0, (float)t.x, a0), p.score_log2, -m_use));
+          float pr1 = exp2_fast(__builtin_fmaf(__builtin_fmaf(a1, (float)t.y, a1), p.score_log2, -m_use));
+          if constexpr (MASK) {
+            pr0 = (a0 == ninf()) ? 0.f : pr0;
+            pr1 = (a1 == ninf()) ? 0.f : pr1;
+          }
+          sacc[mt][r] = pr0;
+          sacc[mt][r + 1] = pr1;
         }
-        sacc[mt][r] = pr;
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < BN / 32; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = sacc[mt][r];
+          float pr;
+          if constexpr (SOFTCAP) {
+            const float t = exp2_fast(s * p.tanh_log2);
+            const float rr = rcp_fast(t + 1.f);
+            pr = exp2_fast(__builtin_fmaf(rr, -2.f * p.cap_log2, p.cap_log2 - m_use));
+            if constexpr (MASK) pr = (s == ninf()) ? 0.f : pr;
+          } else {
+            pr = exp2_fast(__builtin_fmaf(s, p.score_log2, -m_use));
+          }
+          sacc[mt][r] = pr;
+        }
       }
     }
 

@@ -48,6 +48,12 @@ SMALL = [
     ("f32_gqa_causal", dict(dtype="f32", hq=8, hkv=2, d=64), [70, 1, 33], [70, 200, 40]),
     ("f32_d128_softcap", dict(dtype="f32", hq=4, hkv=4, d=128, softcap=5.0, causal=False), [40, 3], [17, 90]),
     ("f32_odd_dim", dict(dtype="f32", hq=2, hkv=1, d=40, causal=True), [9, 30], [12, 30]),
+    # Softcap ranges for the MFMA kernel's two tanh forms: every tile inside the
+    # short-series range, tiles on both sides of it, and a very large cap whose
+    # range bound is the f16 clamp.
+    ("bf16_softcap_series_only", dict(hq=8, hkv=2, softcap=50.0, sigma=0.5), [200, 1, 77], [200, 300, 77]),
+    ("bf16_softcap_series_edge", dict(hq=8, hkv=2, softcap=10.0, sigma=1.0), [150, 33], [150, 400]),
+    ("f16_softcap_wide_cap", dict(dtype="f16", hq=8, hkv=2, softcap=1000.0, sigma=3.0), [130, 5], [130, 260]),
 ]
 
 
@@ -213,6 +219,79 @@ def test_full_size_workloads_sampled(name):
     _say("full", name, len(picks), "rows max_abs", ma, "rel_l2", rel)
     assert torch.isfinite(out.float()).all()
     del batch, out
+    torch.cuda.empty_cache()
+
+
+def test_one_16384_key_causal_softcap_sequence_sampled():
+    """A single sequence at the longest length of the long softcap workload
+    (16384 queries and keys, 64 query heads over 8 KV heads, softcap 50,
+    inputs N(0, 1.5)): rows spread over the whole range, at the tile edges
+    and at the end, on every head for some of them, against the oracle."""
+    import torch
+    w = synth.WORKLOADS["long_causal_softcap"]
+    L = 16384
+    _say("single 16384-key sequence", w)
+    batch = synth.make_batch(w, [L], [L], device="cuda")
+    out = run_gpu(batch)
+    rng = np.random.default_rng(5)
+    all_heads = [0, 127, 128, 8191, 16383]
+    rows = sorted(set(all_heads) | {1, 63, 64, 255, 256, 4095, 4096, 12288, 16256, 16320}
+                  | set(rng.integers(0, L, size=24).tolist()))
+    picks = []
+    for r in rows:
+        heads = range(w.num_heads) if r in all_heads else rng.integers(0, w.num_heads, size=4).tolist()
+        picks += [(0, int(r), int(h)) for h in heads]
+    ma, rel = compare(gather_gpu(batch, out, picks), oracle_sampled(batch, picks), w.dtype)
+    _say("single 16384-key sequence", len(picks), "rows max_abs", ma, "rel_l2", rel)
+    assert torch.isfinite(out.float()).all()
+    del batch, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["ragged_causal_prefill", "long_causal_softcap", "chunked_prefill_cache",
+                                  "packed_decode"])
+def test_benchmark_graph_replay_equals_host_call_full_size(name):
+    """The call the benchmark times: varlen_attn_fwd_device on the full-size
+    batch, captured once into a HIP graph after a warm-up on a side stream
+    (decode-only batches fork decode and combine onto the library's side
+    stream inside the capture). Three replays, with eager host-planned calls
+    in between, each equal the host-planned call bit for bit."""
+    import torch
+    import packed_varlen_scaled_amd as pva
+    w = synth.WORKLOADS[name]
+    _say("bench graph", name)
+    batch = synth.workload_batch(name, device="cuda")
+    want = run_gpu(batch).clone()
+    cu_q = torch.from_numpy(batch.cu_q).cuda()
+    cu_kv = torch.from_numpy(batch.cu_kv).cuda()
+    out = torch.empty_like(want)
+    ws, latch = _device_buffers(batch)
+
+    def call():
+        pva.varlen_attn_fwd_device(batch.q, batch.k, batch.v, cu_q, cu_kv, w.num_heads, w.kv_num_heads,
+                                   scale=w.scale or None, is_causal=w.is_causal, softcap=w.softcap, out=out,
+                                   workspace=ws, error_latch=latch)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(latch.item()) == 0
+        assert torch.equal(out, want), (name, rep)
+        assert torch.equal(run_gpu(batch), want), (name, rep)
+    _say("bench graph", name, "3 replays bitwise equal")
+    del g, batch, out, want, ws
     torch.cuda.empty_cache()
 
 
