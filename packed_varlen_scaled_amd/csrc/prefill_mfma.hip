@@ -14,11 +14,11 @@
 // of one kv head (NH * R waves of 64 lanes), keys [kv_begin, kv_end).
 // Each wave owns one query head and 32 query rows. Per key tile of 64 keys:
 //   * the workgroup streams K and V from HBM straight into LDS (global_load_lds,
-//     no staging registers), both as [key][d] with 16-byte chunks permuted
-//     by key so that neither the K fragment reads nor the V transpose reads
-//     collide in LDS banks,
-//     double-buffered, once for all NH heads of the group (the GQA reuse);
-//     one barrier per tile;
+//     no staging registers) in the blocked layout of prefill_tiles.h: loads
+//     coalesce, neither the K fragment reads nor the V transpose reads
+//     collide in LDS banks, and every fragment read is a per-lane base plus
+//     an immediate offset; double-buffered, once for all NH heads of the
+//     group (the GQA reuse); one barrier per tile;
 //   * S^T = K . Q^T on 32x32x16 MFMA: lane l then holds 32 scores of query
 //     row l%32, so a row's max / sum need one exchange between lane halves
 //     (v_permlane32_swap);
@@ -55,16 +55,18 @@ template <int D, int DV, bool BF16, int NW, bool SOFTCAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   constexpr int BN = 64;  // keys per tile
-  using KS = TileShape<D, NW>;
-  using VS = TileShape<DV, NW>;
+  using KL = TileLayout<D>;
+  using VL = TileLayout<DV>;
+  static_assert(KL::BLOCKS % NW == 0 && VL::BLOCKS % NW == 0, "tile blocks must split evenly over the waves");
+  constexpr int KBPW = KL::BLOCKS / NW;  // 1 KB load blocks per wave per tile
+  constexpr int VBPW = VL::BLOCKS / NW;
 
-  // K0 K1 V0 V1, each [key][d] with 16-byte chunk c of row r stored at chunk
-  // c ^ chunk_perm<row width>(r). After the key loop the same bytes stage
-  // each wave's 32 x DV output tile (OST elements per wave).
+  // K0 K1 V0 V1 in the blocked layout of TileLayout. After the key loop the
+  // same bytes stage each wave's 32 x DV output tile (OST elements per wave).
   constexpr int OST = 32 * DV;
-  constexpr int LDS_ELEMS = (2 * KS::TILE + 2 * VS::TILE) > NW * OST ? (2 * KS::TILE + 2 * VS::TILE) : NW * OST;
+  constexpr int LDS_ELEMS = (2 * KL::TILE + 2 * VL::TILE) > NW * OST ? (2 * KL::TILE + 2 * VL::TILE) : NW * OST;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
-  constexpr int V0 = 2 * KS::TILE;  // first V buffer
+  constexpr int V0 = 2 * KL::TILE;  // first V buffer
 
   // Device path: workgroups past the prefill grid run the combine items
   // (their split-KV partials are complete: decode ran before this launch).
@@ -127,65 +129,60 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
 
   // ---- HBM -> LDS tile loads ------------------------------------------------
   // Wave w fills 1 KB blocks w, w + NW, ... of each tile; lane L of a block
-  // lands at byte 16*L of it, i.e. row L / CH of the block, stored chunk
-  // L % CH, so it fetches logical chunk (L % CH) ^ chunk_perm(row).
+  // lands in slot L of it and so fetches the (row, chunk) the layout puts
+  // there.
   const int64_t k_stride = (int64_t)p.hkv * D;   // elements between consecutive tokens
   const int64_t v_stride = (int64_t)p.hkv * DV;
   const char* kbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.k) +
                                                     ((int64_t)it.kv_token0 * p.hkv + g) * D);
   const char* vbase = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) +
                                                     ((int64_t)it.kv_token0 * p.hkv + g) * DV);
-  const int k_row = wave * KS::ROWS_PER_BLOCK + lane / KS::CH;  // row in this wave's first K block
-  const int v_row = wave * VS::ROWS_PER_BLOCK + lane / VS::CH;
-  const uint32_t k_off = (uint32_t)((k_row * k_stride + ((lane % KS::CH) ^ chunk_perm<D>(k_row)) * 8) * 2);
-  const uint32_t v_off = (uint32_t)((v_row * v_stride + ((lane % VS::CH) ^ chunk_perm<DV>(v_row)) * 8) * 2);
-  const uint32_t k_step = (uint32_t)(NW * KS::ROWS_PER_BLOCK * k_stride * 2);  // bytes between this wave's blocks
-  const uint32_t v_step = (uint32_t)(NW * VS::ROWS_PER_BLOCK * v_stride * 2);
+  const int k_row = KL::load_row(wave, lane);  // row in this wave's first K block
+  const int v_row = VL::load_row(wave, lane);
+  const uint32_t k_off = (uint32_t)((k_row * k_stride + KL::load_chunk(lane) * 8) * 2);
+  const uint32_t v_off = (uint32_t)((v_row * v_stride + VL::load_chunk(lane) * 8) * 2);
+  const uint32_t k_step = (uint32_t)(NW * KL::RB * k_stride * 2);  // bytes between this wave's blocks
+  const uint32_t v_step = (uint32_t)(NW * VL::RB * v_stride * 2);
 
   auto issue_tile = [&](int kt, int buf) {
     const char* kb = kbase + (int64_t)kt * k_stride * 2;
     const char* vb = vbase + (int64_t)kt * v_stride * 2;
-    uint16_t* kl = lds + buf * KS::TILE + wave * 512;
-    uint16_t* vl = lds + V0 + buf * VS::TILE + wave * 512;
+    uint16_t* kl = lds + buf * KL::TILE + wave * KL::BLOCK_ELEMS;
+    uint16_t* vl = lds + V0 + buf * VL::TILE + wave * VL::BLOCK_ELEMS;
     const int rows = kv_end - kt;
     // rows at or past kv_end are zeros (never the next sequence)
 #pragma unroll
-    for (int i = 0; i < KS::BPW; ++i) {
-      if (rows >= BN || k_row + i * NW * KS::ROWS_PER_BLOCK < rows) {
-        lds_dma16_async(kb + k_off + i * k_step, lds_addr32(kl + i * NW * 512));
+    for (int i = 0; i < KBPW; ++i) {
+      if (rows >= BN || k_row + i * NW * KL::RB < rows) {
+        lds_dma16_async(kb + k_off + i * k_step, lds_addr32(kl + i * NW * KL::BLOCK_ELEMS));
       } else {
         const u32x4_t zero = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(kl + i * NW * 512 + 8 * lane) = zero;
+        *reinterpret_cast<u32x4_t*>(kl + i * NW * KL::BLOCK_ELEMS + 8 * lane) = zero;
       }
     }
 #pragma unroll
-    for (int i = 0; i < VS::BPW; ++i) {
-      if (rows >= BN || v_row + i * NW * VS::ROWS_PER_BLOCK < rows) {
-        lds_dma16_async(vb + v_off + i * v_step, lds_addr32(vl + i * NW * 512));
+    for (int i = 0; i < VBPW; ++i) {
+      if (rows >= BN || v_row + i * NW * VL::RB < rows) {
+        lds_dma16_async(vb + v_off + i * v_step, lds_addr32(vl + i * NW * VL::BLOCK_ELEMS));
       } else {
         const u32x4_t zero = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(vl + i * NW * 512 + 8 * lane) = zero;
+        *reinterpret_cast<u32x4_t*>(vl + i * NW * VL::BLOCK_ELEMS + 8 * lane) = zero;
       }
     }
   };
 
-  // ---- per-lane LDS read addresses (element offsets in buffer 0) -------------
-  // K fragment of S^T: key row 32*mt + l32, logical chunk 2*kk + half.
-  int k_addr[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) k_addr[kk] = l32 * D + (((2 * kk + half) ^ chunk_perm<D>(l32)) << 3);
+  // ---- per-lane LDS read bases (element offsets within a tile) ---------------
+  // K fragment of S^T: key row 32*mt + l32, chunk 2*kk + half, at
+  // k_lane + k_frag(kk, mt) (a constant).
+  const int k_lane = KL::elem(l32, half);
   // V^T fragments via the transpose read: 16-lane group G covers head dims
-  // 16*(G%2) + 0..15 of keys 4*(G/2) + 0..3 (+8) of each 16-key block.
+  // 16*(G%2) + 0..15 of keys 4*(G/2) + 0..3 (+8) of each 16-key block, at
+  // v_lane + v_frag(kb, mb, h) for key offset 16*kb + 8*h.
   const int trg = lane >> 4;
   const int tr_i = lane & 15;
   const int tr_key = 4 * (trg >> 1) + (tr_i >> 2);
-  int v_addr[DV / 32], v_addr8[DV / 32];  // rows tr_key and tr_key + 8 of each 16-key block
-#pragma unroll
-  for (int mb = 0; mb < DV / 32; ++mb) {
-    const int dd = 32 * mb + 16 * (trg & 1) + 4 * (tr_i & 3);
-    v_addr[mb] = tr_key * DV + (((dd >> 3) ^ chunk_perm<DV>(tr_key)) << 3) + (dd & 7);
-    v_addr8[mb] = (tr_key + 8) * DV + (((dd >> 3) ^ chunk_perm<DV>(tr_key + 8)) << 3) + (dd & 7);
-  }
+  const int tr_d = 16 * (trg & 1) + 4 * (tr_i & 3);
+  const int v_lane = VL::elem(tr_key, tr_d >> 3) + (tr_d & 7);
 
   // One key tile. MODE selects the masking and the softmax bookkeeping:
   //   kFirst  - first tile of the item: masked; sets each row's reference
@@ -201,8 +198,12 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   auto compute = [&](int buf, int kt, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
     constexpr bool MASK = MODE != kPlain;
-    const uint16_t* ks = lds + buf * KS::TILE;
-    const uint16_t* vs = lds + V0 + buf * VS::TILE;
+    const uint16_t* ks = lds + buf * KL::TILE + k_lane;
+    const uint16_t* vs = lds + V0 + buf * VL::TILE + v_lane;
+    // fragment offsets from the lane bases: the row steps are multiples of
+    // the block height and the chunk steps keep the in-block swizzle
+    constexpr auto k_frag = [](int kk, int mt) { return KL::elem(32 * mt, 2 * kk) - KL::elem(0, 0); };
+    constexpr auto v_frag = [](int kb, int mb, int h) { return VL::elem(16 * kb + 8 * h, 4 * mb) - VL::elem(0, 0); };
 
     // ---- S^T = K Q^T -------------------------------------------------------
     // K fragments stream through a ring of KPF register slots, KPF - 1 steps
@@ -216,7 +217,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     auto load_k = [&](int kk) {
 #pragma unroll
       for (int mt = 0; mt < BN / 32; ++mt)
-        kfr[kk % KPF][mt] = *reinterpret_cast<const u32x4_t*>(ks + k_addr[kk] + 32 * mt * D);
+        kfr[kk % KPF][mt] = *reinterpret_cast<const u32x4_t*>(ks + k_frag(kk, mt));
     };
 #pragma unroll
     for (int kk = 0; kk < KPF - 1 && kk < KSTEPS; ++kk) load_k(kk);
@@ -396,8 +397,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       u32x4_t a[DV / 32];
 #pragma unroll
       for (int mb = 0; mb < DV / 32; ++mb) {
-        const u32x2_t lo = lds_read_tr16(vs + v_addr[mb] + 16 * kb * DV);
-        const u32x2_t hi = lds_read_tr16(vs + v_addr8[mb] + 16 * kb * DV);
+        const u32x2_t lo = lds_read_tr16(vs + v_frag(kb, mb, 0));
+        const u32x2_t hi = lds_read_tr16(vs + v_frag(kb, mb, 1));
         a[mb] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
       }
 #pragma unroll
