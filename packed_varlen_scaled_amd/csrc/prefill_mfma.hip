@@ -102,10 +102,9 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const int kv_end = it.kv_end;
   const int64_t tok = (int64_t)it.q_token0 + it.q_row_begin + my_row;
   // Short-series softcap (see the tile body): x = a * cap_k for a raw score
-  // a; usable while |a| <= cap_short_lim (|x| <= 1/4, and a within f16).
-  // The series is even in x, so a negative cap takes it too.
+  // a, usable while x^2 <= 1/16. The series is even in x, so a negative cap
+  // takes it too.
   const float cap_kf = SOFTCAP ? p.scale / p.softcap : 0.f;
-  const float cap_short_lim = SOFTCAP ? fminf(0.25f / __builtin_fabsf(cap_kf), 32768.f) : 0.f;
   const f16x2_t cap_k = {(_Float16)cap_kf, (_Float16)cap_kf};
   const f16x2_t cap_c1 = {(_Float16)(-1.f / 3.f), (_Float16)(-1.f / 3.f)};
   const f16x2_t cap_c2 = {(_Float16)(2.f / 15.f), (_Float16)(2.f / 15.f)};
@@ -239,17 +238,31 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     // the bf16 rounding of P. This takes one transcendental per score instead
     // of three (2^x, reciprocal, 2^x). The form is chosen per wave and tile:
     // every raw score of the wave's tile (masked ones included, taken before
-    // the mask) must lie within the bound, else the tile takes the exact
-    // form. The bound also keeps the raw scores inside f16's range.
+    // the mask) must give x^2 <= 1/16 in f16, else the tile takes the exact
+    // form. x^2 of each register pair is formed here once, in packed f16, and
+    // reused by the series; its maximum takes 8 v_pk_maximum3_f16. A score
+    // outside f16's range, or a NaN, fails the test (maximum keeps NaN).
     bool short_cap = false;
-    if constexpr (SOFTCAP && (MODE == kPlain || MODE == kMasked)) {
-      float mx = 0.f;
+    [[maybe_unused]] f16x2_t cap_u[BN / 32][8];
+    if constexpr (SOFTCAP && MODE != kSafe) {
 #pragma unroll
       for (int mt = 0; mt < BN / 32; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, __builtin_fabsf(sacc[mt][r])), __builtin_fabsf(sacc[mt][r + 1]));
+        for (int r = 0; r < 16; r += 2) {
+          const f16x2_t x = __builtin_convertvector(f32x2_t{sacc[mt][r], sacc[mt][r + 1]}, f16x2_t) * cap_k;
+          cap_u[mt][r / 2] = x * x;
+        }
       }
-      short_cap = !__any(!(mx <= cap_short_lim));
+      f16x2_t um = cap_u[0][0];
+#pragma unroll
+      for (int i = 1; i < BN / 2; i += 2) {
+        const f16x2_t b = cap_u[i / 8][i % 8];
+        um = (i + 1 < BN / 2) ? __builtin_elementwise_maximum(__builtin_elementwise_maximum(um, b),
+                                                              cap_u[(i + 1) / 8][(i + 1) % 8])
+                              : __builtin_elementwise_maximum(um, b);
+      }
+      const float umax = (float)__builtin_elementwise_maximum(um.x, um.y);
+      short_cap = !__any(!(umax <= 0.0625f));
     }
 
     // ---- mask and tile max ---------------------------------------------------
@@ -333,15 +346,14 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
 
     // ---- P = 2^(y - m_use) -----------------------------------------------------
     if (short_cap) {
-      // y = score_log2 * a * (1 + t), a the raw score, t from x = a * scale / c
-      // in packed f16 (a masked score is -inf and gives P = 0 either way)
+      // y = score_log2 * a * (1 + t), a the raw score, t from u = x^2 in
+      // packed f16 (a masked score is -inf and gives P = 0 either way)
 #pragma unroll
       for (int mt = 0; mt < BN / 32; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float a0 = sacc[mt][r], a1 = sacc[mt][r + 1];
-          const f16x2_t x = __builtin_convertvector(f32x2_t{a0, a1}, f16x2_t) * cap_k;
-          const f16x2_t u = x * x;
+          const f16x2_t u = cap_u[mt][r / 2];
           const f16x2_t t = u * (u * cap_c2 + cap_c1);
           float pr0 = exp2_fast(__builtin_fmaf(__builtin_fmaf(a0, (float)t.x, a0), p.score_log2, -m_use));
           float pr1 = exp2_fast(__builtin_fmaf(__builtin_fmaf(a1, (float)t.y, a1), p.score_log2, -m_use));
