@@ -4,6 +4,8 @@
 // conversion, cross-lane exchange).
 #pragma once
 
+#include <utility>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -261,6 +263,34 @@ __device__ __forceinline__ void lds_dma16_async(const void* gsrc, uint32_t lds_b
       : "v"(gsrc), "s"(lds_base)
       : "memory", "m0");
 }
+// The same in the scalar-base form: global address sbase + voff (a 32-bit
+// per-lane offset), M0 = lds_base + OFF with the constant folded into the
+// instruction that sets M0. A run of loads from one tile then needs one
+// 64-bit scalar base and one M0 base instead of an address pair and an M0
+// value per load. gfx950 reads a vector memory instruction's scalar
+// operands at issue, so the base may be overwritten right after.
+template <uint32_t OFF>
+__device__ __forceinline__ void lds_dma16_async_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base), "i"(OFF)
+      : "memory", "m0", "scc");
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a constant
+// expression in f.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // LDS byte address of a pointer into a __shared__ array (wave-uniform when
 // the pointer is).
 __device__ __forceinline__ uint32_t lds_addr32(const void* p) {

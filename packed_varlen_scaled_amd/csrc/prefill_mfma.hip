@@ -143,16 +143,48 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const uint32_t k_step = (uint32_t)(NW * KL::RB * k_stride * 2);  // bytes between this wave's blocks
   const uint32_t v_step = (uint32_t)(NW * VL::RB * v_stride * 2);
 
+  // LDS byte addresses of this wave's first K and V block in buffer 0 (the
+  // generic-to-LDS pointer conversion is done once, not per load).
+  const uint32_t k_lds0 = lds_addr32(lds) + wave * KL::BLOCK_ELEMS * 2;
+  const uint32_t v_lds0 = lds_addr32(lds) + (V0 + wave * VL::BLOCK_ELEMS) * 2;
+  const uint32_t k_row_bytes = (uint32_t)(k_stride * 2);
+  const uint32_t v_row_bytes = (uint32_t)(v_stride * 2);
+  // this lane's byte offset within a tile for each of the wave's blocks
+  uint32_t k_voff[KBPW], v_voff[VBPW];
+#pragma unroll
+  for (int i = 0; i < KBPW; ++i) k_voff[i] = k_off + i * k_step;
+#pragma unroll
+  for (int i = 0; i < VBPW; ++i) v_voff[i] = v_off + i * v_step;
+
+  // All 8 (or 4) waves issue a tile's loads right after the same barrier, and
+  // their scalar instructions share the CU's one scalar unit, so the common
+  // case - a whole tile inside kv_end, decided per workgroup - is kept to a
+  // few scalar operations per load. kt >= 0, so the 32 x 32-bit product is
+  // the byte offset.
   auto issue_tile = [&](int kt, int buf) {
-    const char* kb = kbase + (int64_t)kt * k_stride * 2;
-    const char* vb = vbase + (int64_t)kt * v_stride * 2;
+    const char* kb = kbase + (uint64_t)(uint32_t)kt * k_row_bytes;
+    const char* vb = vbase + (uint64_t)(uint32_t)kt * v_row_bytes;
+    const int rows = kv_end - kt;
+    if (rows >= BN) {
+      const uint32_t km0 = k_lds0 + buf * (KL::TILE * 2);
+      const uint32_t vm0 = v_lds0 + buf * (VL::TILE * 2);
+      static_for<KBPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        lds_dma16_async_sv<i * NW * KL::BLOCK_ELEMS * 2>(kb, k_voff[i], km0);
+      });
+      static_for<VBPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        lds_dma16_async_sv<i * NW * VL::BLOCK_ELEMS * 2>(vb, v_voff[i], vm0);
+      });
+      return;
+    }
+    // The item's last tile: rows at or past kv_end are zeros (never the next
+    // sequence).
     uint16_t* kl = lds + buf * KL::TILE + wave * KL::BLOCK_ELEMS;
     uint16_t* vl = lds + V0 + buf * VL::TILE + wave * VL::BLOCK_ELEMS;
-    const int rows = kv_end - kt;
-    // rows at or past kv_end are zeros (never the next sequence)
 #pragma unroll
     for (int i = 0; i < KBPW; ++i) {
-      if (rows >= BN || k_row + i * NW * KL::RB < rows) {
+      if (k_row + i * NW * KL::RB < rows) {
         lds_dma16_async(kb + k_off + i * k_step, lds_addr32(kl + i * NW * KL::BLOCK_ELEMS));
       } else {
         const u32x4_t zero = {0u, 0u, 0u, 0u};
@@ -161,7 +193,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     }
 #pragma unroll
     for (int i = 0; i < VBPW; ++i) {
-      if (rows >= BN || v_row + i * NW * VL::RB < rows) {
+      if (v_row + i * NW * VL::RB < rows) {
         lds_dma16_async(vb + v_off + i * v_step, lds_addr32(vl + i * NW * VL::BLOCK_ELEMS));
       } else {
         const u32x4_t zero = {0u, 0u, 0u, 0u};
