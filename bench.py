@@ -64,8 +64,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 DEFAULT_WORKLOAD = "long_causal_softcap"
 SUB_WORKLOADS = ("long_causal_softcap", "ragged_causal_prefill", "chunked_prefill_cache", "packed_decode")
 KERNEL_SOURCES = {
-    "prefill_mfma": ["packed_varlen_scaled_amd/csrc/prefill_mfma.hip", "packed_varlen_scaled_amd/csrc/common.h"],
-    "decode": ["packed_varlen_scaled_amd/csrc/decode.hip", "packed_varlen_scaled_amd/csrc/common.h"],
+    "prefill_mfma": ["packed_varlen_scaled_amd/csrc/prefill_mfma.hip", "packed_varlen_scaled_amd/csrc/prefill_tiles.h",
+                     "packed_varlen_scaled_amd/csrc/combine.h", "packed_varlen_scaled_amd/csrc/common.h"],
+    "decode": ["packed_varlen_scaled_amd/csrc/decode.hip", "packed_varlen_scaled_amd/csrc/combine.h",
+               "packed_varlen_scaled_amd/csrc/common.h"],
     "cache_step": ["packed_varlen_scaled_amd/csrc/rope_append.hip", "packed_varlen_scaled_amd/csrc/common.h"],
 }
 CACHE_WORKLOADS = ("packed_decode", "chunked_prefill_cache")

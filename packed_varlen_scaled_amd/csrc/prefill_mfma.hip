@@ -164,10 +164,10 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   auto issue_tile = [&](int kt, int buf) {
     const char* kb = kbase + (uint64_t)(uint32_t)kt * k_row_bytes;
     const char* vb = vbase + (uint64_t)(uint32_t)kt * v_row_bytes;
+    const uint32_t km0 = k_lds0 + buf * (KL::TILE * 2);
+    const uint32_t vm0 = v_lds0 + buf * (VL::TILE * 2);
     const int rows = kv_end - kt;
     if (rows >= BN) {
-      const uint32_t km0 = k_lds0 + buf * (KL::TILE * 2);
-      const uint32_t vm0 = v_lds0 + buf * (VL::TILE * 2);
       static_for<KBPW>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         lds_dma16_async_sv<i * NW * KL::BLOCK_ELEMS * 2>(kb, k_voff[i], km0);
@@ -178,28 +178,27 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       });
       return;
     }
-    // The item's last tile: rows at or past kv_end are zeros (never the next
-    // sequence).
-    uint16_t* kl = lds + buf * KL::TILE + wave * KL::BLOCK_ELEMS;
-    uint16_t* vl = lds + V0 + buf * VL::TILE + wave * VL::BLOCK_ELEMS;
-#pragma unroll
-    for (int i = 0; i < KBPW; ++i) {
+    // The item's last tile: lanes whose row lies at or past kv_end write
+    // zeros instead (never the next sequence's data).
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    uint16_t* kl = lds + buf * KL::TILE + wave * KL::BLOCK_ELEMS + 8 * lane;
+    uint16_t* vl = lds + V0 + buf * VL::TILE + wave * VL::BLOCK_ELEMS + 8 * lane;
+    static_for<KBPW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       if (k_row + i * NW * KL::RB < rows) {
-        lds_dma16_async(kb + k_off + i * k_step, lds_addr32(kl + i * NW * KL::BLOCK_ELEMS));
+        lds_dma16_async_sv<i * NW * KL::BLOCK_ELEMS * 2>(kb, k_voff[i], km0);
       } else {
-        const u32x4_t zero = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(kl + i * NW * KL::BLOCK_ELEMS + 8 * lane) = zero;
+        *reinterpret_cast<u32x4_t*>(kl + i * NW * KL::BLOCK_ELEMS) = zero;
       }
-    }
-#pragma unroll
-    for (int i = 0; i < VBPW; ++i) {
+    });
+    static_for<VBPW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       if (v_row + i * NW * VL::RB < rows) {
-        lds_dma16_async(vb + v_off + i * v_step, lds_addr32(vl + i * NW * VL::BLOCK_ELEMS));
+        lds_dma16_async_sv<i * NW * VL::BLOCK_ELEMS * 2>(vb, v_voff[i], vm0);
       } else {
-        const u32x4_t zero = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(vl + i * NW * VL::BLOCK_ELEMS + 8 * lane) = zero;
+        *reinterpret_cast<u32x4_t*>(vl + i * NW * VL::BLOCK_ELEMS) = zero;
       }
-    }
+    });
   };
 
   // ---- per-lane LDS read bases (element offsets within a tile) ---------------
