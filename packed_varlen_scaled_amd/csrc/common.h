@@ -239,36 +239,21 @@ __device__ __forceinline__ float sum2(uint32_t w, float acc) {
   }
 }
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
-// lane i's bytes land at ldst + 16*i, ldst being uniform across the wave.
-__device__ __forceinline__ void lds_dma16(const void* gsrc, void* ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, ldst, 16, 0, 0);
-}
-
-// The same load issued as inline assembly (M0 = lds_base, which must be
-// wave-uniform; lane i's bytes land at lds_base + 16*i). The compiler then
-// does not count it among the wave's outstanding vector-memory loads, so it
-// adds no vmcnt wait of its own before later LDS reads (it cannot tell which
-// LDS bytes such a load writes and would otherwise wait after every one).
-// Whoever issues it orders it explicitly: an s_waitcnt vmcnt covering the
-// load, then a workgroup barrier, before any wave reads the bytes. The
-// compiler's own vmcnt waits stay correct (loads retire in order, so an
-// extra load issued in between only makes them wait longer).
-__device__ __forceinline__ void lds_dma16_async(const void* gsrc, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(gsrc), "s"(lds_base)
-      : "memory", "m0");
-}
-// The same in the scalar-base form: global address sbase + voff (a 32-bit
-// per-lane offset), M0 = lds_base + OFF with the constant folded into the
-// instruction that sets M0. A run of loads from one tile then needs one
-// 64-bit scalar base and one M0 base instead of an address pair and an M0
-// value per load. gfx950 reads a vector memory instruction's scalar
-// operands at issue, so the base may be overwritten right after.
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4 in its scalar-base form): lane i reads
+// sbase + voff_i and its bytes land at M0 + 16*i, with M0 = lds_base + OFF
+// (wave-uniform; the constant is folded into the instruction that sets M0,
+// so a run of loads into one buffer needs one scalar register, not one per
+// load). gfx950 reads a vector memory instruction's scalar operands at
+// issue, so the base may be overwritten right after.
+// Issued as inline assembly, the load is not among the outstanding
+// vector-memory loads the compiler counts, so it adds no vmcnt wait of its
+// own before later LDS reads (it cannot tell which LDS bytes such a load
+// writes and would otherwise wait after every one). Whoever issues it orders
+// it explicitly: an s_waitcnt vmcnt covering the load, then a workgroup
+// barrier, before any wave reads the bytes. The compiler's own vmcnt waits
+// stay correct (loads retire in order, so an extra load issued in between
+// only makes them wait longer).
 template <uint32_t OFF>
 __device__ __forceinline__ void lds_dma16_async_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
   asm volatile(
