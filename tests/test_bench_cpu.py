@@ -100,3 +100,27 @@ def test_headline_is_the_largest_workload_and_sub_records_cover_the_rest():
         sizes[name] = 2.0 * pairs * w.num_heads * (w.head_dim + w.dv)
     assert bench.DEFAULT_WORKLOAD == max(sizes, key=sizes.get)
     assert set(bench.SUB_WORKLOADS) == set(synth.WORKLOADS) - {"tiny_fp32"}
+
+
+def test_kernel_source_hash_covers_every_local_include():
+    """The traffic counters in profiles/ are used only while the hash of the
+    kernel's sources matches; every header a kernel file includes from the
+    package (transitively) must be part of that hash."""
+    import re
+    csrc = os.path.join(os.path.dirname(bench.__file__), "packed_varlen_scaled_amd", "csrc")
+
+    def closure(name, seen):
+        if name in seen:
+            return seen
+        seen.add(name)
+        with open(os.path.join(csrc, name)) as f:
+            for inc in re.findall(r'^#include "([^"]+)"', f.read(), flags=re.M):
+                if os.path.exists(os.path.join(csrc, inc)):
+                    closure(inc, seen)
+        return seen
+
+    for kind, files in bench.KERNEL_SOURCES.items():
+        names = {os.path.basename(f) for f in files}
+        main = [n for n in names if n.endswith(".hip")]
+        assert len(main) == 1, (kind, names)
+        assert closure(main[0], set()) <= names, (kind, closure(main[0], set()) - names)
