@@ -217,6 +217,8 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   // One key tile. MODE selects the masking and the softmax bookkeeping:
   //   kFirst  - first tile of the item: masked; sets each row's reference
   //             max m_ref, against which every later P is taken;
+  //   kFirstOpen - the same for a first tile that every row of the
+  //             workgroup sees whole (no key masked), without the mask;
   //   kPlain  - a tile that needs no mask for any row of the workgroup;
   //   kMasked - a tile that crosses the causal frontier, a window edge or
   //             kv_end;
@@ -227,7 +229,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   // rescaled and no max is taken inside the loop.
   auto compute = [&](int buf, int kt, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
-    constexpr bool MASK = MODE != kPlain;
+    constexpr bool MASK = MODE != kPlain && MODE != kFirstOpen;
     const uint16_t* ks = lds + buf * KL::TILE + k_lane;
     const uint16_t* vs = lds + V0 + buf * VL::TILE + v_lane;
     // fragment offsets from the lane bases: the row steps are multiples of
@@ -324,7 +326,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
         }
       }
     }
-    if constexpr (MODE == kFirst || MODE == kSafe) {
+    if constexpr (MODE == kFirst || MODE == kFirstOpen || MODE == kSafe) {
       float mx = ninf();
 #pragma unroll
       for (int mt = 0; mt < BN / 32; ++mt) {
@@ -339,7 +341,7 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       } else {
         tmax = mx * p.score_log2;
       }
-      if constexpr (MODE == kFirst) {
+      if constexpr (MODE == kFirst || MODE == kFirstOpen) {
         m_ref = tmax;
       } else {
         const float m_new = fmaxf(m_ref, tmax);
@@ -463,9 +465,13 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
     t_plain1 = min(t_plain1, max(0, (frontier - kv_begin) / BN));
   }
   int t_plain0 = 1;
+  // The first tile needs no mask when it is whole, before the first row's
+  // causal frontier and, with a window, not before the last row's window start.
+  bool first_open = t_plain1 >= 1;
   if (p.window > 0) {
     const int lo_last = it.q_row_begin + it.q_rows - 1 + off + 1 - p.window;  // last row's window start
     t_plain0 = max(1, (lo_last - kv_begin + BN - 1) / BN);
+    first_open = first_open && lo_last <= kv_begin;
   }
   // This wave's rows see none of the keys of the tile at kt.
   auto skips = [&](int kt) {
@@ -492,7 +498,13 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
       // reaches past tile 1 for some row (only items of 128 rows) gets no
       // plain region: a third loop instantiation of the tile body makes the
       // compiler move the accumulators to scratch memory.
-      if (n_tiles > 0) compute(0, step(0), std::integral_constant<int, kFirst>{});
+      if (n_tiles > 0) {
+        if (first_open) {
+          compute(0, step(0), std::integral_constant<int, kFirstOpen>{});
+        } else {
+          compute(0, step(0), std::integral_constant<int, kFirst>{});
+        }
+      }
       const int p1 = t_plain0 > 1 ? 1 : max(1, min(t_plain1, n_tiles));
       for (int t = 1; t < p1; ++t) compute(t & 1, step(t), std::integral_constant<int, kPlain>{});
       for (int t = p1; t < n_tiles; ++t) {

@@ -7,7 +7,7 @@
 
 namespace pva {
 
-enum TileMode : int { kFirst = 0, kPlain = 1, kMasked = 2, kSafe = 3 };
+enum TileMode : int { kFirst = 0, kPlain = 1, kMasked = 2, kSafe = 3, kFirstOpen = 4 };
 
 // LDS layout of a 64-key tile whose rows hold W 16-bit elements (CH = W / 8
 // chunks of 16 bytes). One global_load_lds instruction fills one 1 KB block
