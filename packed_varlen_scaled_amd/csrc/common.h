@@ -30,7 +30,7 @@ struct WorkItem {
   int32_t len_q;         // L_q
   int32_t len_kv;        // L_kv
   int32_t split;         // index of this split in [0, n_splits)
-  int32_t pad;
+  int32_t kv_head;       // kv head of the item's query heads: head_begin / group
 };
 static_assert(sizeof(WorkItem) == 64, "work item is 16 int32");
 
@@ -77,7 +77,7 @@ enum LatchBits : int32_t {
   kLatchKvLen = 1024,     // attention over a cache: a length is negative or exceeds the capacity
 };
 struct DevicePlan {
-  int32_t batch, hq;
+  int32_t batch, hq, group;  // group = hq / hkv
   int32_t nh, rows_per_item, prefill_kind;  // prefill items: nh heads x rows_per_item rows
   int32_t nh_dec, use_decode;               // decode items: nh_dec heads, L_q == 1 sequences
   int32_t causal, window;

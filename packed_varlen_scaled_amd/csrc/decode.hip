@@ -62,7 +62,7 @@ void decode_kernel(Params p, const WorkItem* __restrict__ items) {
   const int n = lane & 15;     // query head slot within the item
   const bool slot_ok = n < it.heads;
   const int head = it.head_begin + (slot_ok ? n : 0);
-  const int g = it.head_begin / p.group;
+  const int g = it.kv_head;
   const int i_local = it.q_row_begin;  // the single query row
   const int off = it.len_kv - it.len_q;
   const int kv_end = it.kv_end;

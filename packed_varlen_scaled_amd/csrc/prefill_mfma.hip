@@ -82,10 +82,12 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int hh = wave % it.heads;
-  const int rb = wave / it.heads;
+  // it.heads is a power of two (the schedulers take the largest one that
+  // divides the GQA group, up to 8): no division at item start
+  const int hh = wave & (it.heads - 1);
+  const int rb = wave >> __builtin_ctz(it.heads);
   const int head = it.head_begin + hh;
-  const int g = it.head_begin / p.group;
+  const int g = it.kv_head;
   const int row0 = rb * 32;
   const int my_row = row0 + l32;
   const bool row_ok = my_row < it.q_rows;
@@ -111,13 +113,15 @@ void prefill_mfma_kernel(Params p, const WorkItem* __restrict__ items) {
 
   // Q fragments, the B operand of S^T = K Q^T: lane l supplies query row
   // l%32 at head dims 16*kk + 8*half + 0..7.
+  // (one masked region for all of them: rows past the tile load nothing)
   u32x4_t qf[D / 16];
-  {
-    const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) qf[kk] = u32x4_t{0u, 0u, 0u, 0u};
+  if (row_ok) {
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
         static_cast<const uint16_t*>(p.q) + (tok * p.hq + head) * D);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = row_ok ? src[2 * kk + half] : zero;
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = src[2 * kk + half];
   }
 
   f32x16_t oacc[DV / 32];

@@ -424,7 +424,7 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
     it.len_q = aq[b + 1] - aq[b];
     it.len_kv = lkv_of(b);
     it.split = 0;
-    it.pad = 0;
+    it.kv_head = 0;
     return it;
   };
   auto make_pre = [&](int32_t k) {
@@ -438,6 +438,7 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
     it.q_rows = min(dp.rows_per_item, it.len_q - it.q_row_begin);
     it.head_begin = (j % g_pre) * dp.nh;
     it.heads = dp.nh;
+    it.kv_head = it.head_begin / dp.group;
     it.kv_begin = visible_begin_dev(it.len_q, it.len_kv, it.q_row_begin, dp.window);
     it.kv_end = max(it.kv_begin, visible_end_dev(it.len_q, it.len_kv, it.q_row_begin, it.q_rows, dp.causal));
     return it;
@@ -456,6 +457,7 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
     it.q_rows = 1;
     it.head_begin = gi * dp.nh_dec;
     it.heads = dp.nh_dec;
+    it.kv_head = it.head_begin / dp.group;
     if (r.ns == 1) {
       it.kv_begin = r.vb;
       it.kv_end = r.ve;
@@ -476,6 +478,7 @@ __device__ void plan_body(const DevicePlan& dp, const int32_t* __restrict__ cu_q
     it.q_rows = 1;
     it.head_begin = gi * dp.nh_dec;
     it.heads = dp.nh_dec;
+    it.kv_head = it.head_begin / dp.group;
     it.partial_base = apart[b] + gi * r.ns * dp.nh_dec;
     it.n_splits = r.ns;
     it.kv_begin = r.vb;

@@ -320,6 +320,7 @@ varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
           it.q_rows = rows;
           it.head_begin = h;
           it.heads = 1;
+          it.kv_head = h / pr.group;
           it.kv_begin = kv_begin;
           it.kv_end = kv_end;
           plan.f32.push_back(it);
@@ -365,6 +366,7 @@ varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
           it.q_rows = 1;
           it.head_begin = h0;
           it.heads = nh_dec;
+          it.kv_head = h0 / pr.group;
           const int32_t kv_begin = visible_begin(proto, 0, pr.window);
           const int32_t kv_end = std::max(kv_begin, visible_end(proto, 0, 1, causal));
           emit_split(plan, plan.decode, it, kv_begin, kv_end, dchunk);
@@ -382,6 +384,7 @@ varlen_status_t build_plan(const Problem& pr, const Options& opt, Plan& plan) {
           it.q_rows = rows;
           it.head_begin = h0;
           it.heads = nh;
+          it.kv_head = h0 / pr.group;
           emit_split(plan, plan.prefill, it, kv_begin, kv_end,
                      pchunk > 0 ? pchunk : std::max<int32_t>(kv_end - kv_begin, 1));
           plan.visited_pairs_x_heads += (int64_t)rows * (kv_end - kv_begin) * nh;
@@ -787,6 +790,7 @@ varlen_status_t run_device(const void* q, const void* k, const void* v, const in
   std::memset(&dp, 0, sizeof dp);
   dp.batch = pr.batch;
   dp.hq = pr.hq;
+  dp.group = pr.group;
   dp.nh = sh.nh;
   dp.rows_per_item = sh.rows_per_item;
   dp.prefill_kind = sh.prefill_kind;
