@@ -22,6 +22,13 @@
 //   * S^T = K . Q^T on 32x32x16 MFMA: lane l then holds 32 scores of query
 //     row l%32, so a row's max / sum need one exchange between lane halves
 //     (v_permlane32_swap);
+//   * softcap c*tanh(s/c) (the row kernel's softcap stage): on a tile whose
+//     scores all have |s/c| <= 1/4, as s*(1 - x^2/3 + 2x^4/15), x = s/c, in
+//     packed f16 (one transcendental per score); otherwise the exact form
+//     from 2^x and a reciprocal;
+//   * the mask only on tiles that cross kv_end, the causal frontier or a
+//     window edge for some row of the workgroup (an item's first tile, too,
+//     only when some row does not see all of it);
 //   * softmax in registers in log2 units (exp2 with log2(e) folded into the
 //     scale). Each row's first tile fixes a reference max and every later P
 //     is taken against it, so O is never rescaled and no tile max is taken
